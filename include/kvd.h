@@ -1,0 +1,186 @@
+/*
+ * kvd.h -- C ABI of the KV-cached decode-attention library (libkvd.so),
+ * hand-written HIP kernels for MI355X (gfx950).
+ *
+ * The operation is the single-token decode step of a decoder layer's
+ * attention as the ferric-core `examples/generate.rs` page defines it (module
+ * doc comment; `step_gpu`): the new token's Q and K are rotated by RoPE at the
+ * token's absolute position, the new K/V rows are appended to the per-layer
+ * cache, and each query attends against the whole cache (`mha_decode_t`, which
+ * takes separate query-head and kv-head counts).  The Ferrum Infer README
+ * ("Key Optimizations") adds what a serving batch needs: per-item positions in
+ * one launch, one launch for all batch items, a paged block pool addressed
+ * through a block table, and split-K flash decoding for long caches.  The
+ * ferrox-models index (`speculative`) adds verifying several draft tokens per
+ * sequence in one batched pass.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch-owned
+ *     memory on the current device) unless a comment says otherwise; the
+ *     descriptor itself lives in host memory and is read during the call only.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises, and keeps no state between calls except a per-thread error
+ *     string and a per-device cache of the compute-unit count.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  It launches kernels and returns.
+ *   - Arguments are validated on the host first.  On any error nothing is
+ *     enqueued and a non-zero kvd_status is returned; kvd_last_error() then
+ *     describes it.  Device-side contract violations (a block id outside the
+ *     pool, seq_lens[b] above max_seq_len) are undefined behaviour.
+ */
+#ifndef KVD_H
+#define KVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (int32_t on the wire). */
+enum {
+    KVD_OK = 0,
+    KVD_ERR_NULL = 1,        /* a required pointer is NULL */
+    KVD_ERR_SHAPE = 2,       /* inconsistent sizes */
+    KVD_ERR_UNSUPPORTED = 3, /* valid but not built (head_dim, dtype, ...) */
+    KVD_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+    KVD_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
+};
+
+/* Cache element types. */
+enum { KVD_KV_F32 = 0, KVD_KV_BF16 = 1 };
+
+/* RoPE pairings (the pages name a configurable RoPE layout in the ferrox
+ * `config` module without defining it): HALF rotates (x[i], x[i + D/2]),
+ * INTERLEAVED rotates (x[2i], x[2i + 1]), for i < D/2. */
+enum { KVD_ROPE_HALF = 0, KVD_ROPE_INTERLEAVED = 1 };
+
+/* Attention kernel families (kvd_attn_options.kernel). */
+enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
+
+/*
+ * The paged KV cache of one layer plus the batch it serves.
+ *
+ *   num_seqs            B, sequences in the batch (>= 0; 0 is a no-op).
+ *   q_tokens_per_seq    T, new tokens per sequence: 1 = decode, >1 = verify of
+ *                       a T-token draft, causal within the draft.  1..16.
+ *   n_q_heads           Hq; n_kv_heads Hkv; Hq % Hkv == 0.  Query head h
+ *                       reads kv head h / (Hq / Hkv).
+ *   head_dim            D in {16, 32, 64, 128, 256}.
+ *   block_size          bs, keys per cache block: a power of two, 1..1024.
+ *   num_blocks          blocks in each pool.
+ *   max_blocks_per_seq  row stride of block_table.
+ *   max_seq_len         host-side upper bound on every seq_lens[b]; it sizes
+ *                       the split-K plan (no device read is needed, so a call
+ *                       can be captured in a HIP graph).
+ *                       T <= max_seq_len <= max_blocks_per_seq * bs.
+ *   kv_dtype            KVD_KV_BF16 or KVD_KV_F32.
+ *   k_cache, v_cache    [num_blocks][Hkv][bs][D] each, element type kv_dtype,
+ *                       16-byte aligned.  Key position p of sequence b lives in
+ *                       block block_table[b][p / bs], slot p % bs.
+ *   block_table         int32 [B][max_blocks_per_seq], physical block ids.
+ *   seq_lens            int32 [B]: keys of each sequence INCLUDING its T new
+ *                       tokens (seq_lens[b] >= T).  New token t of sequence b
+ *                       sits at position seq_lens[b] - T + t and its query
+ *                       sees keys 0 .. seq_lens[b] - T + t.
+ */
+typedef struct kvd_paged_kv {
+    int32_t num_seqs;
+    int32_t q_tokens_per_seq;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t max_blocks_per_seq;
+    int32_t max_seq_len;
+    int32_t kv_dtype;
+    void *k_cache;
+    void *v_cache;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+} kvd_paged_kv;
+
+/*
+ * RoPE + append (generate.rs `step_gpu`: `rope_off_t` on q and k at the token's
+ * position, then the K/V rows are appended; Ferrum README: batched RoPE with
+ * per-item positions, paged KV writes).
+ *
+ *   q      fp32 [B][T][Hq][D]  new queries before RoPE.
+ *   k, v   fp32 [B][T][Hkv][D] new keys (before RoPE) and values.
+ *   q_rot  fp32 [B][T][Hq][D]  rotated queries (may alias q).
+ *   rope_base  theta_i = rope_base^(-2i/D); position p turns pair i by p*theta_i.
+ *   layout     KVD_ROPE_HALF or KVD_ROPE_INTERLEAVED.
+ *
+ * Angles and rotations are evaluated in fp64; q_rot is that value rounded to
+ * fp32, the cache receives it rounded to kv_dtype (round-to-nearest-even, a
+ * single rounding), and v is stored rounded to kv_dtype.  Exactly the B*T
+ * target slots of each pool are written.  Only seq_lens, block_table and the
+ * pools are read from the descriptor's device memory.
+ */
+int32_t kvd_rope_append_kv(const kvd_paged_kv *kv, const float *q, const float *k,
+                           const float *v, float *q_rot, double rope_base,
+                           int32_t layout, void *stream);
+
+/* Tuning / testing knobs for decode attention.  A NULL pointer means all
+ * automatic.  num_splits: 0 = automatic, else the number of key-range
+ * partitions per (sequence, kv head).  kernel: KVD_KERNEL_*. */
+typedef struct kvd_attn_options {
+    int32_t num_splits;
+    int32_t kernel;
+} kvd_attn_options;
+
+/* Bytes of device workspace kvd_decode_attention needs for this descriptor on
+ * the current device (0 when no split-K partials are needed).  Returns
+ * (size_t)-1 for an invalid descriptor. */
+size_t kvd_decode_attention_workspace_size(const kvd_paged_kv *kv);
+size_t kvd_decode_attention_workspace_size_ex(const kvd_paged_kv *kv,
+                                              const kvd_attn_options *opt);
+
+/* The plan kvd_decode_attention would use: key-range partitions per (seq, kv
+ * head), keys per partition and kernel family.  Any out pointer may be NULL. */
+int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options *opt,
+                                  int32_t *num_splits, int32_t *keys_per_split,
+                                  int32_t *kernel);
+
+/*
+ * Decode attention over the paged cache (generate.rs `mha_decode_t`; Ferrum
+ * README: one launch for every batch item, block-table indirection, split-K
+ * flash decoding with an online-softmax combine; ferrox `speculative`: all
+ * draft tokens verified in one pass).
+ *
+ *   q_rot          fp32 [B][T][Hq][D] rotated queries.
+ *   out            fp32 [B][T][Hq][D]
+ *                  out = sum_j softmax_j(scale * q.K_j) V_j over the visible
+ *                  keys j = 0 .. seq_lens[b] - T + t.
+ *   softmax_scale  scale; 0 means 1/sqrt(D).
+ *   workspace      device scratch of at least kvd_decode_attention_workspace_size
+ *                  bytes (may be NULL when that is 0), 256-byte aligned.  Its
+ *                  contents need no initialisation and are clobbered.
+ *
+ * Accumulation is fp32; the cache is read in kv_dtype.  Cache slots past
+ * seq_lens (tail slots, unused blocks) are never read, whatever they hold.
+ * For a fixed plan the result is bitwise deterministic (no atomics).
+ */
+int32_t kvd_decode_attention(const kvd_paged_kv *kv, const float *q_rot, float *out,
+                             float softmax_scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
+int32_t kvd_decode_attention_ex(const kvd_paged_kv *kv, const float *q_rot, float *out,
+                                float softmax_scale, const kvd_attn_options *opt,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *kvd_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread (static or
+ * thread-local storage; "" if none). */
+const char *kvd_last_error(void);
+
+/* ABI version, bumped on any incompatible change. */
+int32_t kvd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVD_H */

@@ -1,0 +1,265 @@
+"""Thin ctypes binding over libkvd.so (include/kvd.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libkvd.so.  PyTorch provides device memory and the stream; the
+functions take torch CUDA (HIP) tensors, check their dtype, device, shape and
+contiguity, and pass raw pointers plus torch's current stream to the C ABI.
+There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvd.so")
+
+KVD_OK, KVD_ERR_NULL, KVD_ERR_SHAPE, KVD_ERR_UNSUPPORTED, KVD_ERR_WORKSPACE, KVD_ERR_LAUNCH = range(6)
+KVD_KV_F32, KVD_KV_BF16 = 0, 1
+KVD_ROPE_HALF, KVD_ROPE_INTERLEAVED = 0, 1
+KVD_KERNEL_AUTO, KVD_KERNEL_VALU, KVD_KERNEL_MFMA = 0, 1, 2
+
+EXPORTED = [
+    "kvd_rope_append_kv", "kvd_decode_attention", "kvd_decode_attention_ex",
+    "kvd_decode_attention_workspace_size", "kvd_decode_attention_workspace_size_ex",
+    "kvd_decode_attention_plan", "kvd_status_string", "kvd_last_error", "kvd_abi_version",
+]
+
+
+class KvdPagedKV(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("q_tokens_per_seq", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+class KvdAttnOptions(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+
+
+class KvdError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__(f"{where}: {status_name(status)}: {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkvd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m kv_cached_decode_amd.build` "
+                               "(there is no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        KV = ctypes.POINTER(KvdPagedKV)
+        OPT = ctypes.POINTER(KvdAttnOptions)
+        L.kvd_rope_append_kv.argtypes = [KV, P, P, P, P, ctypes.c_double, I32, P]
+        L.kvd_rope_append_kv.restype = I32
+        L.kvd_decode_attention.argtypes = [KV, P, P, ctypes.c_float, P, SZ, P]
+        L.kvd_decode_attention.restype = I32
+        L.kvd_decode_attention_ex.argtypes = [KV, P, P, ctypes.c_float, OPT, P, SZ, P]
+        L.kvd_decode_attention_ex.restype = I32
+        L.kvd_decode_attention_workspace_size.argtypes = [KV]
+        L.kvd_decode_attention_workspace_size.restype = SZ
+        L.kvd_decode_attention_workspace_size_ex.argtypes = [KV, OPT]
+        L.kvd_decode_attention_workspace_size_ex.restype = SZ
+        L.kvd_decode_attention_plan.argtypes = [KV, OPT, ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                                ctypes.POINTER(I32)]
+        L.kvd_decode_attention_plan.restype = I32
+        L.kvd_status_string.argtypes = [I32]
+        L.kvd_status_string.restype = ctypes.c_char_p
+        L.kvd_last_error.argtypes = []
+        L.kvd_last_error.restype = ctypes.c_char_p
+        L.kvd_abi_version.restype = I32
+        _lib = L
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return lib().kvd_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().kvd_last_error().decode()
+
+
+def _check(status, where):
+    if status != KVD_OK:
+        raise KvdError(status, where, last_error())
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+@dataclass
+class PagedKV:
+    """One layer's paged KV cache plus the batch it serves (kvd_paged_kv).
+
+    k_cache, v_cache: [num_blocks][Hkv][bs][D], torch.bfloat16 or torch.float32.
+    block_table:      int32 [B][max_blocks_per_seq].
+    seq_lens:         int32 [B], keys per sequence including the T new tokens.
+    max_seq_len:      host-side bound on seq_lens (sizes the split-K plan).
+    """
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+    n_q_heads: int
+    q_tokens_per_seq: int
+    max_seq_len: int
+
+    def __post_init__(self):
+        if self.k_cache.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("cache must be bfloat16 or float32")
+        _need(self.k_cache, "k_cache", self.k_cache.dtype)
+        _need(self.v_cache, "v_cache", self.k_cache.dtype, self.k_cache.shape)
+        _need(self.block_table, "block_table", torch.int32)
+        _need(self.seq_lens, "seq_lens", torch.int32)
+        if self.k_cache.dim() != 4 or self.block_table.dim() != 2 or self.seq_lens.dim() != 1:
+            raise ValueError("k/v_cache must be 4-D, block_table 2-D and seq_lens 1-D")
+        if self.block_table.shape[0] != self.seq_lens.shape[0]:
+            raise ValueError("block_table and seq_lens disagree on the batch size")
+
+    @property
+    def num_seqs(self):
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def n_kv_heads(self):
+        return int(self.k_cache.shape[1])
+
+    @property
+    def block_size(self):
+        return int(self.k_cache.shape[2])
+
+    @property
+    def head_dim(self):
+        return int(self.k_cache.shape[3])
+
+    def struct(self) -> KvdPagedKV:
+        return KvdPagedKV(
+            self.num_seqs, int(self.q_tokens_per_seq), int(self.n_q_heads), self.n_kv_heads,
+            self.head_dim, self.block_size, int(self.k_cache.shape[0]),
+            int(self.block_table.shape[1]), int(self.max_seq_len),
+            KVD_KV_BF16 if self.k_cache.dtype == torch.bfloat16 else KVD_KV_F32,
+            self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.block_table.data_ptr(),
+            self.seq_lens.data_ptr())
+
+    def q_shape(self):
+        return (self.num_seqs, self.q_tokens_per_seq, self.n_q_heads, self.head_dim)
+
+    def kv_shape(self):
+        return (self.num_seqs, self.q_tokens_per_seq, self.n_kv_heads, self.head_dim)
+
+
+def _opts(num_splits, kernel):
+    if not num_splits and not kernel:
+        return None
+    return ctypes.byref(KvdAttnOptions(int(num_splits), int(kernel)))
+
+
+def rope_append_kv(kv: PagedKV, q, k, v, q_rot=None, rope_base=10000.0, layout=KVD_ROPE_HALF,
+                   stream=None):
+    """kvd_rope_append_kv: rotate q/k at each new token's position, append the
+    new K/V rows to the cache.  Returns q_rot (allocated if not given)."""
+    _need(q, "q", torch.float32, kv.q_shape())
+    _need(k, "k", torch.float32, kv.kv_shape())
+    _need(v, "v", torch.float32, kv.kv_shape())
+    if q_rot is None:
+        q_rot = torch.empty_like(q)
+    _need(q_rot, "q_rot", torch.float32, kv.q_shape())
+    d = kv.struct()
+    _check(lib().kvd_rope_append_kv(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    q_rot.data_ptr(), float(rope_base), int(layout),
+                                    _stream_handle(stream)), "kvd_rope_append_kv")
+    return q_rot
+
+
+def decode_attention_workspace_size(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO) -> int:
+    d = kv.struct()
+    n = lib().kvd_decode_attention_workspace_size_ex(ctypes.byref(d), _opts(num_splits, kernel))
+    if n == ctypes.c_size_t(-1).value:
+        raise KvdError(KVD_ERR_SHAPE, "kvd_decode_attention_workspace_size", last_error())
+    return int(n)
+
+
+def decode_attention_plan(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO):
+    """(splits, keys per split, kernel family) the library would use."""
+    d = kv.struct()
+    s, kps, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().kvd_decode_attention_plan(ctypes.byref(d), _opts(num_splits, kernel),
+                                           ctypes.byref(s), ctypes.byref(kps), ctypes.byref(k)),
+           "kvd_decode_attention_plan")
+    return s.value, kps.value, k.value
+
+
+_ws_cache = {}
+
+
+def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO):
+    """A cached device workspace big enough for this descriptor (None if none
+    is needed).  Allocation happens here, outside the library."""
+    n = decode_attention_workspace_size(kv, num_splits, kernel)
+    if n == 0:
+        return None
+    dev = kv.k_cache.device
+    buf = _ws_cache.get(dev)
+    if buf is None or buf.numel() < n:
+        buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        _ws_cache[dev] = buf
+    return buf
+
+
+def decode_attention(kv: PagedKV, q_rot, out=None, softmax_scale=0.0, workspace_buf=None,
+                     num_splits=0, kernel=KVD_KERNEL_AUTO, stream=None):
+    """kvd_decode_attention(_ex): out[b,t,h] = softmax(scale q.K^T) V over the
+    keys query t of sequence b can see.  Returns out."""
+    _need(q_rot, "q_rot", torch.float32, kv.q_shape())
+    if out is None:
+        out = torch.empty_like(q_rot)
+    _need(out, "out", torch.float32, kv.q_shape())
+    if workspace_buf is None:
+        workspace_buf = workspace(kv, num_splits, kernel)
+    wptr = workspace_buf.data_ptr() if workspace_buf is not None else None
+    wbytes = workspace_buf.numel() * workspace_buf.element_size() if workspace_buf is not None else 0
+    d = kv.struct()
+    _check(lib().kvd_decode_attention_ex(ctypes.byref(d), q_rot.data_ptr(), out.data_ptr(),
+                                         float(softmax_scale), _opts(num_splits, kernel), wptr,
+                                         wbytes, _stream_handle(stream)),
+           "kvd_decode_attention")
+    return out

@@ -1,0 +1,293 @@
+// attn_valu.hip -- decode attention on the vector ALUs (single-token decode,
+// and the generic path for any row count).
+//
+// The operation is `mha_decode_t` of ferric-core generate.rs (`step_gpu`): the
+// query rows of one sequence attend against every key of its cache; query
+// head h reads kv head h / (Hq/Hkv) (GQA, ferrox `decoder` module).  The
+// Ferrum Infer README ("Key Optimizations") supplies the rest of the shape:
+// one launch for all batch items, block-table indirection into a paged pool,
+// and split-K (flash decoding) for long caches.
+//
+// Work decomposition: one workgroup (4 wave64s) per (split, kv head [x row
+// tile], sequence).  The workgroup streams its key range in steps; within a
+// step each wave owns U "groups" of KPG keys.  A group is one 16-byte
+// global_load_dwordx4 per lane: LPK = 16*D/(16 bytes) lanes share one key row
+// (for bf16, D = 128: 16 lanes x 8 elements), so every load instruction reads
+// KPG whole rows, contiguous and 16-byte aligned.  The same registers feed
+// every query row of the GQA group (K/V are read from HBM once per group).
+//
+//   QK:  each lane forms the partial dot product of its 8 (bf16) or 4 (fp32)
+//        elements with every query row, then an xor butterfly over the LPK
+//        lanes of the key (DPP quad_perm / half_mirror / mirror, then
+//        ds_swizzle-class shuffles for 32/64) leaves the full score in all of
+//        them, bitwise identical.
+//   softmax: online, in log2 units (scale*log2(e) folded into q).  Each lane
+//        group keeps its own running max m, sum l and output o for the keys it
+//        has seen; m is only raised when a score exceeds it by more than TAU
+//        (2^TAU headroom in fp32), so the rescale branch is rare.
+//   PV:  the V registers are in the same lane layout, so o += p * v needs no
+//        data movement.
+//   merge: groups of a wave merge by shuffles, the four waves through LDS;
+//        the workgroup writes either the final row (one split) or its
+//        unnormalised partial (m, l, o) for the combine kernel.
+//
+// Keys past the sequence end are never loaded (their slots may hold NaN);
+// keys past a draft token's own position get score -inf and weight 0.
+#include "kvd_internal.h"
+
+namespace kvd {
+namespace {
+
+constexpr int WAVES = 4;
+constexpr int U = 8;              // groups per wave per step
+constexpr float TAU = 8.0f;       // lazy-rescale headroom, log2 units
+constexpr float M_EMPTY = -1e30f; // running max before any key is seen
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPK consecutive lanes; every lane of a group
+// ends with the same bits (each butterfly stage adds the same two values).
+template <int LPK>
+__device__ inline float group_sum(float x) {
+    if constexpr (LPK >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (LPK >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPK >= 8) x += dpp<0x141>(x);   // row_half_mirror: i <-> 7 - i
+    if constexpr (LPK >= 16) x += dpp<0x140>(x);  // row_mirror: i <-> 15 - i
+    if constexpr (LPK >= 32) x += __shfl_xor(x, 16);
+    if constexpr (LPK >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <int KV, int EPL>
+__device__ inline void to_f32(const uint4& r, float (&f)[EPL]) {
+    if constexpr (KV) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+}
+
+template <int D, int KV, int RT>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+    constexpr int ESZ = KV ? 2 : 4;
+    constexpr int EPL = 16 / ESZ;        // elements per lane per key
+    constexpr int LPK = D / EPL;         // lanes per key
+    constexpr int KPG = 64 / LPK;        // keys per group
+    constexpr int WAVE_KEYS = U * KPG;
+    static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "unsupported head_dim");
+
+    __shared__ float sm_o[WAVES][RT][D];
+    __shared__ float sm_m[WAVES][RT];
+    __shared__ float sm_l[WAVES][RT];
+
+    const CacheView& c = a.c;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x;
+    const int kvh = blockIdx.y % c.Hkv;
+    const int rtile = blockIdx.y / c.Hkv;
+    const int b = blockIdx.z;
+
+    const int L = c.seq_lens[b];
+    const int key_begin = split * a.split_keys;
+    if (key_begin >= L) return;               // empty split: the combine skips it
+    const int key_end = min(L, key_begin + a.split_keys);
+
+    const int kslot = lane / LPK;
+    const int chunk = lane % LPK;
+    const int row0 = rtile * RT;
+
+    // q rows of this tile, pre-scaled into log2 units; row r = t*g + hg.
+    float qv[RT][EPL];
+    int vis[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int row = row0 + r;
+        const bool ok = row < a.rows;
+        const int t = ok ? row / c.g : 0;
+        const int h = kvh * c.g + (ok ? row - t * c.g : 0);
+        vis[r] = ok ? L - c.T + t : -1;       // last visible key (inclusive)
+        const float* qp = a.q + (((size_t)b * c.T + t) * c.Hq + h) * D + chunk * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[r][e] = ok ? qp[e] * a.scale_log2 : 0.0f;
+    }
+
+    float m[RT], l[RT], o[RT][EPL];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        m[r] = M_EMPTY;
+        l[r] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[r][e] = 0.0f;
+    }
+
+    const char* kbase = (const char*)c.k;
+    const char* vbase = (const char*)c.v;
+    const int* trow = c.table + (size_t)b * c.max_blocks;
+    const int bs_mask = (1 << c.log2_bs) - 1;
+    const size_t row_bytes = (size_t)D * ESZ;
+
+    for (int base = key_begin + wave * WAVE_KEYS; base < key_end; base += WAVES * WAVE_KEYS) {
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * KPG + kslot;
+            if (j < key_end) {
+                const int blk = trow[j >> c.log2_bs];
+                const size_t slot = ((((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (j & bs_mask));
+                const size_t off = slot * row_bytes + (size_t)chunk * 16;
+                kr[u] = *(const uint4*)(kbase + off);
+                vr[u] = *(const uint4*)(vbase + off);
+            } else {
+                kr[u] = make_uint4(0, 0, 0, 0);
+                vr[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * KPG + kslot;
+            float kf[EPL];
+            to_f32<KV, EPL>(kr[u], kf);
+            float s[RT];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc += qv[r][e] * kf[e];
+                s[r] = group_sum<LPK>(acc);
+                if (j >= key_end || j > vis[r]) s[r] = -INFINITY;
+            }
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                if (s[r] > m[r] + TAU) {              // rare: raise the running max
+                    const float alpha = exp2f(m[r] - s[r]);
+                    l[r] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+                    m[r] = s[r];
+                }
+            }
+            float vf[EPL];
+            to_f32<KV, EPL>(vr[u], vf);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const float p = exp2f(s[r] - m[r]);
+                l[r] += p;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[r][e] += p * vf[e];
+            }
+        }
+    }
+
+    // merge the KPG key groups of this wave (lanes chunk + LPK*kslot)
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float mo = __shfl_xor(m[r], off);
+            const float lo = __shfl_xor(l[r], off);
+            const float mn = fmaxf(m[r], mo);
+            const float as = exp2f(m[r] - mn), bs = exp2f(mo - mn);
+            l[r] = l[r] * as + lo * bs;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float oo = __shfl_xor(o[r][e], off);
+                o[r][e] = o[r][e] * as + oo * bs;
+            }
+            m[r] = mn;
+        }
+    }
+    if (kslot == 0) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_o[wave][r][chunk * EPL + e] = o[r][e];
+            if (chunk == 0) {
+                sm_m[wave][r] = m[r];
+                sm_l[wave][r] = l[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // merge the four waves and write the row (one split) or the partial
+    for (int idx = threadIdx.x; idx < RT * D; idx += blockDim.x) {
+        const int r = idx / D, d = idx - r * D;
+        const int row = row0 + r;
+        if (row >= a.rows) continue;
+        float M = sm_m[0][r];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm_m[w][r]);
+        float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float f = exp2f(sm_m[w][r] - M);
+            Ls += sm_l[w][r] * f;
+            O += sm_o[w][r][d] * f;
+        }
+        const int t = row / c.g;
+        const int h = kvh * c.g + (row - t * c.g);
+        const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h;
+        if (a.num_splits == 1) {
+            a.out[qrow * D + d] = O / Ls;
+        } else {
+            a.part_o[(qrow * a.num_splits + split) * D + d] = O;
+            if (d == 0) {
+                a.part_ml[(qrow * a.num_splits + split) * 2 + 0] = M;
+                a.part_ml[(qrow * a.num_splits + split) * 2 + 1] = Ls;
+            }
+        }
+    }
+}
+
+template <int D, int KV>
+hipError_t launch_rt(const AttnArgs& a, dim3 grid, hipStream_t s) {
+    switch (a.row_tile) {
+        case 1: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 2>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 4>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 8>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int KV>
+hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
+    switch (a.c.D) {
+        case 16: return launch_rt<16, KV>(a, grid, s);
+        case 32: return launch_rt<32, KV>(a, grid, s);
+        case 64: return launch_rt<64, KV>(a, grid, s);
+        case 128: return launch_rt<128, KV>(a, grid, s);
+        case 256: return launch_rt<256, KV>(a, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int valu_step_keys(int D, int kv_bf16) {
+    const int lpk = D / (kv_bf16 ? 8 : 4);
+    return WAVES * U * (64 / lpk);
+}
+
+int valu_max_row_tile(int, int) { return 8; }
+
+hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s) {
+    const int n_rtiles = (a.rows + a.row_tile - 1) / a.row_tile;
+    dim3 grid(a.num_splits, a.c.Hkv * n_rtiles, a.c.B);
+    return a.kv_bf16 ? launch_d<1>(a, grid, s) : launch_d<0>(a, grid, s);
+}
+
+}  // namespace kvd

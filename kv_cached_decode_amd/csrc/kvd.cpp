@@ -1,0 +1,323 @@
+// kvd.cpp -- the C ABI of libkvd.so: host-side validation, split-K planning
+// and kernel dispatch.  Declarations and the contract of every entry point
+// are in include/kvd.h.
+#include "kvd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kvd_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int32_t ok() {
+    g_err[0] = '\0';
+    return KVD_OK;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, cached per device.
+int num_cus() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+int32_t check_desc(const kvd_paged_kv* kv) {
+    if (!kv) return fail(KVD_ERR_NULL, "descriptor is NULL");
+    if (kv->num_seqs < 0) return fail(KVD_ERR_SHAPE, "num_seqs = %d < 0", kv->num_seqs);
+    if (kv->num_seqs == 0) return KVD_OK;
+    if (kv->q_tokens_per_seq < 1 || kv->q_tokens_per_seq > 16)
+        return fail(kv->q_tokens_per_seq < 1 ? KVD_ERR_SHAPE : KVD_ERR_UNSUPPORTED,
+                    "q_tokens_per_seq = %d (supported 1..16)", kv->q_tokens_per_seq);
+    if (kv->n_q_heads < 1 || kv->n_kv_heads < 1)
+        return fail(KVD_ERR_SHAPE, "head counts must be >= 1 (Hq=%d, Hkv=%d)", kv->n_q_heads,
+                    kv->n_kv_heads);
+    if (kv->n_q_heads % kv->n_kv_heads != 0)
+        return fail(KVD_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0 (%d, %d)", kv->n_q_heads,
+                    kv->n_kv_heads);
+    const int D = kv->head_dim;
+    if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256)
+        return fail(KVD_ERR_UNSUPPORTED, "head_dim = %d (supported 16, 32, 64, 128, 256)", D);
+    if (!is_pow2(kv->block_size) || kv->block_size > 1024)
+        return fail(KVD_ERR_UNSUPPORTED, "block_size = %d (supported powers of two 1..1024)",
+                    kv->block_size);
+    if (kv->num_blocks < 1 || kv->max_blocks_per_seq < 1)
+        return fail(KVD_ERR_SHAPE, "num_blocks = %d, max_blocks_per_seq = %d", kv->num_blocks,
+                    kv->max_blocks_per_seq);
+    if (kv->max_seq_len < kv->q_tokens_per_seq)
+        return fail(KVD_ERR_SHAPE, "max_seq_len = %d < q_tokens_per_seq = %d", kv->max_seq_len,
+                    kv->q_tokens_per_seq);
+    if ((int64_t)kv->max_seq_len > (int64_t)kv->max_blocks_per_seq * kv->block_size)
+        return fail(KVD_ERR_SHAPE, "max_seq_len = %d exceeds max_blocks_per_seq * block_size = %lld",
+                    kv->max_seq_len, (long long)kv->max_blocks_per_seq * kv->block_size);
+    if (kv->kv_dtype != KVD_KV_F32 && kv->kv_dtype != KVD_KV_BF16)
+        return fail(KVD_ERR_UNSUPPORTED, "kv_dtype = %d", kv->kv_dtype);
+    if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens)
+        return fail(KVD_ERR_NULL, "k_cache, v_cache, block_table and seq_lens must be non-NULL");
+    if (((uintptr_t)kv->k_cache | (uintptr_t)kv->v_cache) & 15)
+        return fail(KVD_ERR_SHAPE, "k_cache and v_cache must be 16-byte aligned");
+    if (((uintptr_t)kv->block_table | (uintptr_t)kv->seq_lens) & 3)
+        return fail(KVD_ERR_SHAPE, "block_table and seq_lens must be 4-byte aligned");
+    return KVD_OK;
+}
+
+kvd::CacheView view_of(const kvd_paged_kv* kv) {
+    kvd::CacheView c;
+    c.B = kv->num_seqs;
+    c.T = kv->q_tokens_per_seq;
+    c.Hq = kv->n_q_heads;
+    c.Hkv = kv->n_kv_heads;
+    c.D = kv->head_dim;
+    c.g = kv->n_q_heads / kv->n_kv_heads;
+    c.log2_bs = ilog2(kv->block_size);
+    c.max_blocks = kv->max_blocks_per_seq;
+    c.table = kv->block_table;
+    c.seq_lens = kv->seq_lens;
+    c.k = kv->k_cache;
+    c.v = kv->v_cache;
+    return c;
+}
+
+struct Plan {
+    int kernel;       // KVD_KERNEL_VALU / KVD_KERNEL_MFMA
+    int splits;
+    int split_keys;
+    int rows;
+    int row_tile;
+};
+
+// Split-K plan from host-known sizes only (graph-capture safe).  Aim for a
+// few thousand workgroups so that every CU streams, with at least MIN_STEPS
+// kernel steps of keys per split so the partials stay small next to the
+// cache reads.
+int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) {
+    const int D = kv->head_dim;
+    const int bf16 = kv->kv_dtype == KVD_KV_BF16;
+    const int g = kv->n_q_heads / kv->n_kv_heads;
+    p->rows = g * kv->q_tokens_per_seq;
+    int kernel = opt ? opt->kernel : KVD_KERNEL_AUTO;
+    if (kernel != KVD_KERNEL_AUTO && kernel != KVD_KERNEL_VALU && kernel != KVD_KERNEL_MFMA)
+        return fail(KVD_ERR_UNSUPPORTED, "kernel = %d", kernel);
+    const bool mfma_ok = kvd::mfma_supported(D, bf16, p->rows);
+    if (kernel == KVD_KERNEL_MFMA && !mfma_ok)
+        return fail(KVD_ERR_UNSUPPORTED,
+                    "MFMA kernel needs a bf16 cache, head_dim 128 and g*T <= 16 (rows = %d)",
+                    p->rows);
+    if (kernel == KVD_KERNEL_AUTO) kernel = (mfma_ok && kv->q_tokens_per_seq > 1) ? KVD_KERNEL_MFMA
+                                                                                 : KVD_KERNEL_VALU;
+    p->kernel = kernel;
+
+    int step, n_rtiles;
+    if (kernel == KVD_KERNEL_MFMA) {
+        step = kvd::mfma_step_keys();
+        p->row_tile = 16;
+        n_rtiles = 1;
+    } else {
+        step = kvd::valu_step_keys(D, bf16);
+        const int max_rt = kvd::valu_max_row_tile(D, bf16);
+        int rt = 1;
+        while (rt < p->rows && rt < max_rt) rt <<= 1;
+        p->row_tile = rt;
+        n_rtiles = (int)cdiv(p->rows, rt);
+    }
+    const int64_t max_len = kv->max_seq_len;
+    const int64_t max_splits = cdiv(max_len, step);
+    int64_t splits;
+    if (opt && opt->num_splits > 0) {
+        splits = opt->num_splits;
+    } else {
+        const int64_t units = (int64_t)kv->num_seqs * kv->n_kv_heads * n_rtiles;
+        const int64_t target = 8LL * num_cus();
+        const int64_t MIN_STEPS = 2;
+        splits = cdiv(target, units);
+        splits = std::min<int64_t>(splits, cdiv(max_len, MIN_STEPS * step));
+        if (splits < 1) splits = 1;
+    }
+    splits = std::min<int64_t>(splits, max_splits);
+    if (splits < 1) splits = 1;
+    int64_t keys = cdiv(cdiv(max_len, splits), step) * step;
+    splits = cdiv(max_len, keys);
+    if (splits > 65535) return fail(KVD_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)splits);
+    p->splits = (int)splits;
+    p->split_keys = (int)keys;
+    return KVD_OK;
+}
+
+size_t workspace_for(const kvd_paged_kv* kv, const Plan& p) {
+    if (p.splits <= 1) return 0;
+    const size_t rows = (size_t)kv->num_seqs * kv->q_tokens_per_seq * kv->n_q_heads;
+    size_t o = rows * p.splits * kv->head_dim * sizeof(float);
+    o = (o + 255) & ~size_t(255);
+    return o + rows * p.splits * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvd_abi_version(void) { return 1; }
+
+const char* kvd_status_string(int32_t s) {
+    switch (s) {
+        case KVD_OK: return "KVD_OK";
+        case KVD_ERR_NULL: return "KVD_ERR_NULL";
+        case KVD_ERR_SHAPE: return "KVD_ERR_SHAPE";
+        case KVD_ERR_UNSUPPORTED: return "KVD_ERR_UNSUPPORTED";
+        case KVD_ERR_WORKSPACE: return "KVD_ERR_WORKSPACE";
+        case KVD_ERR_LAUNCH: return "KVD_ERR_LAUNCH";
+        default: return "KVD_ERR_UNKNOWN";
+    }
+}
+
+const char* kvd_last_error(void) { return g_err; }
+
+int32_t kvd_rope_append_kv(const kvd_paged_kv* kv, const float* q, const float* k, const float* v,
+                           float* q_rot, double rope_base, int32_t layout, void* stream) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (kv->num_seqs == 0) return ok();
+    if (!q || !k || !v || !q_rot) return fail(KVD_ERR_NULL, "q, k, v and q_rot must be non-NULL");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)q_rot) & 3)
+        return fail(KVD_ERR_SHAPE, "q, k, v, q_rot must be 4-byte aligned");
+    if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+        return fail(KVD_ERR_SHAPE, "rope_base must be finite and > 0");
+    if (layout != KVD_ROPE_HALF && layout != KVD_ROPE_INTERLEAVED)
+        return fail(KVD_ERR_UNSUPPORTED, "rope layout = %d", layout);
+    kvd::RopeAppendArgs a;
+    a.c = view_of(kv);
+    a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
+    a.interleaved = layout == KVD_ROPE_INTERLEAVED;
+    a.base = rope_base;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_rot = q_rot;
+    hipError_t e = kvd::launch_rope_append(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "rope_append_kv launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t kvd_decode_attention_workspace_size_ex(const kvd_paged_kv* kv, const kvd_attn_options* opt) {
+    if (check_desc(kv) != KVD_OK) return (size_t)-1;
+    if (kv->num_seqs == 0) return 0;
+    Plan p;
+    if (make_plan(kv, opt, &p) != KVD_OK) return (size_t)-1;
+    return workspace_for(kv, p);
+}
+
+size_t kvd_decode_attention_workspace_size(const kvd_paged_kv* kv) {
+    return kvd_decode_attention_workspace_size_ex(kv, nullptr);
+}
+
+int32_t kvd_decode_attention_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt,
+                                  int32_t* num_splits, int32_t* keys_per_split, int32_t* kernel) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (kv->num_seqs == 0) {
+        if (num_splits) *num_splits = 0;
+        if (keys_per_split) *keys_per_split = 0;
+        if (kernel) *kernel = KVD_KERNEL_VALU;
+        return ok();
+    }
+    Plan p;
+    st = make_plan(kv, opt, &p);
+    if (st != KVD_OK) return st;
+    if (num_splits) *num_splits = p.splits;
+    if (keys_per_split) *keys_per_split = p.split_keys;
+    if (kernel) *kernel = p.kernel;
+    return ok();
+}
+
+int32_t kvd_decode_attention_ex(const kvd_paged_kv* kv, const float* q_rot, float* out,
+                                float softmax_scale, const kvd_attn_options* opt, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (kv->num_seqs == 0) return ok();
+    if (!q_rot || !out) return fail(KVD_ERR_NULL, "q_rot and out must be non-NULL");
+    if (((uintptr_t)q_rot | (uintptr_t)out) & 3)
+        return fail(KVD_ERR_SHAPE, "q_rot and out must be 4-byte aligned");
+    if (!std::isfinite(softmax_scale))
+        return fail(KVD_ERR_SHAPE, "softmax_scale must be finite");
+    Plan p;
+    st = make_plan(kv, opt, &p);
+    if (st != KVD_OK) return st;
+    const size_t need = workspace_for(kv, p);
+    if (need > 0) {
+        if (!workspace) return fail(KVD_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+        if (workspace_bytes < need)
+            return fail(KVD_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+        if ((uintptr_t)workspace & 255) return fail(KVD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    const double scale = softmax_scale != 0.0f ? (double)softmax_scale : 1.0 / std::sqrt((double)kv->head_dim);
+    kvd::AttnArgs a;
+    a.c = view_of(kv);
+    a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
+    a.num_splits = p.splits;
+    a.split_keys = p.split_keys;
+    a.rows = p.rows;
+    a.row_tile = p.row_tile;
+    a.scale_log2 = (float)(scale * 1.4426950408889634);
+    a.q = q_rot;
+    a.out = out;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    if (p.splits > 1) {
+        const size_t rows = (size_t)kv->num_seqs * kv->q_tokens_per_seq * kv->n_q_heads;
+        size_t o = rows * p.splits * kv->head_dim * sizeof(float);
+        o = (o + 255) & ~size_t(255);
+        a.part_o = (float*)workspace;
+        a.part_ml = (float*)((char*)workspace + o);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s) : kvd::launch_attn_valu(a, s);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "decode attention launch: %s", hipGetErrorString(e));
+    if (p.splits > 1) {
+        e = kvd::launch_attn_combine(a, s);
+        if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+int32_t kvd_decode_attention(const kvd_paged_kv* kv, const float* q_rot, float* out,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return kvd_decode_attention_ex(kv, q_rot, out, softmax_scale, nullptr, workspace, workspace_bytes,
+                                   stream);
+}
+
+}  // extern "C"

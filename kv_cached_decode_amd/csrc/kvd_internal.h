@@ -1,0 +1,60 @@
+// kvd_internal.h -- launch parameters shared by the host dispatcher (kvd.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+// Everything a kernel needs about the paged cache and the batch.
+struct CacheView {
+    int32_t B, T, Hq, Hkv, D;
+    int32_t g;              // Hq / Hkv
+    int32_t log2_bs;        // block size is a power of two
+    int32_t max_blocks;     // block_table row stride
+    const int32_t* table;   // [B][max_blocks]
+    const int32_t* seq_lens;  // [B]
+    void* k;                // [num_blocks][Hkv][bs][D]
+    void* v;
+};
+
+struct RopeAppendArgs {
+    CacheView c;
+    int32_t kv_bf16;
+    int32_t interleaved;
+    double base;
+    const float* q;
+    const float* k;
+    const float* v;
+    float* q_rot;
+};
+
+// One key-range partition per (b, kv head, split); rows of a (b, kv head)
+// pair are the g*T query rows (t, h in group) that read it.
+struct AttnArgs {
+    CacheView c;
+    int32_t kv_bf16;
+    int32_t num_splits;     // S
+    int32_t split_keys;     // keys per split (multiple of the kernel's step)
+    int32_t rows;           // g*T
+    int32_t row_tile;       // rows handled by one workgroup (grid.y = Hkv * row tiles)
+    float scale_log2;       // softmax scale * log2(e)
+    const float* q;         // [B][T][Hq][D]
+    float* out;             // [B][T][Hq][D] (written directly when S == 1)
+    float* part_o;          // [B][T][Hq][S][D]   unnormalised partial outputs
+    float* part_ml;         // [B][T][Hq][S][2]   (running max in log2 units, sum)
+};
+
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
+hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
+
+// Kernel-family properties the planner needs.
+int valu_step_keys(int D, int kv_bf16);      // keys per workgroup step
+int valu_max_row_tile(int D, int kv_bf16);   // rows one workgroup can hold
+bool mfma_supported(int D, int kv_bf16, int rows);
+int mfma_step_keys();
+
+}  // namespace kvd

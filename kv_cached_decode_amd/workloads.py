@@ -28,6 +28,8 @@ kernel that reads or weights them shows it.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional, Tuple, Union
 
@@ -153,11 +155,19 @@ def _draw(rng, n, dist, dtype_out):
     return x
 
 
-def _fill_pool(rng, pool, dist, kv_dtype, chunk=1 << 26):
+def _fill_pool(seed_seq, pool, dist, kv_dtype, chunk=1 << 24):
+    """Fill a pool chunk by chunk, each chunk from its own child generator of
+    seed_seq, so the values do not depend on how many threads draw them."""
     flat = pool.reshape(-1)
-    for i in range(0, flat.size, chunk):
-        n = min(chunk, flat.size - i)
-        flat[i:i + n] = _draw(rng, n, dist, kv_dtype)
+    starts = list(range(0, flat.size, chunk))
+    kids = seed_seq.spawn(len(starts))
+
+    def job(i):
+        n = min(chunk, flat.size - starts[i])
+        flat[starts[i]:starts[i] + n] = _draw(np.random.default_rng(kids[i]), n, dist, kv_dtype)
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(job, range(len(starts))))
 
 
 def _poison_value(kv_dtype, which):
@@ -200,8 +210,9 @@ def make_workload(spec: Spec) -> Workload:
         k_pool[...] = _poison_value(spec.kv_dtype, 0)
         v_pool[...] = _poison_value(spec.kv_dtype, 0)
     else:
-        _fill_pool(rng, k_pool, spec.dist, spec.kv_dtype)
-        _fill_pool(rng, v_pool, spec.dist, spec.kv_dtype)
+        k_seq, v_seq = np.random.SeedSequence([spec.seed, 1]), np.random.SeedSequence([spec.seed, 2])
+        _fill_pool(k_seq, k_pool, spec.dist, spec.kv_dtype)
+        _fill_pool(v_seq, v_pool, spec.dist, spec.kv_dtype)
     # poison every slot at or past the context: the new tokens' slots and the tail
     for b in range(B):
         for pos in range(int(ctx[b]), nblk[b] * bs):

@@ -1,0 +1,116 @@
+"""Helpers for the GPU tests: upload a workload, run the HIP path through the
+C ABI (via the thin binding), run the oracle on the same inputs, compare."""
+import functools
+import sys
+
+import numpy as np
+import torch
+
+from helpers import oracle_cache
+from kv_cached_decode_amd import binding as kb
+from kv_cached_decode_amd import workloads
+
+DEV = "cuda:0"
+
+
+def note(*a):
+    """Name the case before a GPU step (flushed, so a crash still shows it)."""
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev_pool(pool):
+    if pool.dtype == np.uint16:
+        return torch.from_numpy(pool.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(pool).to(DEV)
+
+
+def to_host_pool(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=2)
+def cached_workload(spec):
+    return workloads.make_workload(spec)
+
+
+class GpuCase:
+    """A workload resident on the GPU, ready for the step."""
+
+    def __init__(self, w, seq_lens=None, q_tokens=None):
+        self.w = w
+        s = w.spec
+        self.k_cache = to_dev_pool(w.k_pool)
+        self.v_cache = to_dev_pool(w.v_pool)
+        self.table = torch.from_numpy(w.block_table).to(DEV)
+        sl = w.seq_lens if seq_lens is None else seq_lens
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(sl, dtype=np.int32)).to(DEV)
+        T = q_tokens or s.q_tokens
+        self.kv = kb.PagedKV(self.k_cache, self.v_cache, self.table, self.seq_lens, s.n_q_heads, T,
+                             max(int(np.max(sl)), T) if len(sl) else T)
+        self.q = torch.from_numpy(w.q).to(DEV)
+        self.k = torch.from_numpy(w.k).to(DEV)
+        self.v = torch.from_numpy(w.v).to(DEV)
+
+    def step(self, kernel=kb.KVD_KERNEL_AUTO, num_splits=0, scale=0.0):
+        s = self.w.spec
+        q_rot = kb.rope_append_kv(self.kv, self.q, self.k, self.v, rope_base=s.rope_base,
+                                  layout=s.layout)
+        out = kb.decode_attention(self.kv, q_rot, softmax_scale=scale, num_splits=num_splits,
+                                  kernel=kernel)
+        torch.cuda.synchronize()
+        return q_rot.cpu().numpy(), out.cpu().numpy()
+
+    def attention(self, q_rot, kernel=kb.KVD_KERNEL_AUTO, num_splits=0, scale=0.0):
+        out = kb.decode_attention(self.kv, q_rot, softmax_scale=scale, num_splits=num_splits,
+                                  kernel=kernel)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def pools(self):
+        return to_host_pool(self.k_cache), to_host_pool(self.v_cache)
+
+
+def oracle_step(w, rows=None, scale=None):
+    """Oracle RoPE + append + attention on host copies.  Returns (q_rot fp64,
+    out fp64 for all rows or the given flat rows, k_pool, v_pool)."""
+    s = w.spec
+    oc = oracle_cache(w)
+    q_rot = oc.rope_append_kv(w.q, w.k, w.v, s.rope_base, s.layout)
+    if rows is None:
+        out = oc.decode_attention(q_rot, scale=scale)
+    else:
+        out, _ = oc.decode_attention_rows(q_rot, rows, scale=scale)
+    return q_rot, out, oc.k_pool, oc.v_pool
+
+
+def rel_err(gpu, ref):
+    """Normwise relative error max|gpu - ref| / max|ref| (the bf16 criterion)."""
+    return float(np.max(np.abs(gpu - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def abs_err(gpu, ref):
+    return float(np.max(np.abs(gpu - ref)))
+
+
+def assert_parity(spec, gpu_out, ref_out):
+    """fp32 caches: 1e-5 max-abs; bf16 caches with fp32 accumulation: 2e-3
+    normwise relative."""
+    assert np.all(np.isfinite(gpu_out)), "non-finite output"
+    if spec.kv_dtype == "f32":
+        e = abs_err(gpu_out, ref_out)
+        assert e <= 1e-5, f"{spec.name}: max-abs error {e:.3e} > 1e-5"
+    else:
+        e = rel_err(gpu_out, ref_out)
+        assert e <= 2e-3, f"{spec.name}: normwise relative error {e:.3e} > 2e-3"
+    return e
+
+
+def assert_qrot(gpu_q, ref_q):
+    """q_rot is the fp64 rotation rounded to fp32: within one fp32 rounding."""
+    ref32 = ref_q.astype(np.float32)
+    diff = np.abs(gpu_q.astype(np.float64) - ref_q)
+    bound = np.abs(ref_q) * 2.0 ** -23 + 1e-30
+    assert np.all(diff <= bound), f"q_rot off by more than an fp32 ulp ({np.max(diff / bound):.2f})"
+    return int(np.sum(gpu_q != ref32))

@@ -1,0 +1,153 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry
+point the header declares, and rejects bad descriptors before launching
+anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cached_decode_amd import binding as kb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kb.LIB_PATH), reason="libkvd.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(kb.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(kb.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    assert kb.status_name(0) == "KVD_OK"
+    assert kb.status_name(4) == "KVD_ERR_WORKSPACE"
+    assert kb.status_name(99) == "KVD_ERR_UNKNOWN"
+    assert kb.lib().kvd_abi_version() == 1
+
+
+FAKE = 0x100000   # never dereferenced: every case below fails validation first
+
+
+def desc(**kw):
+    d = dict(num_seqs=2, q_tokens_per_seq=1, n_q_heads=8, n_kv_heads=2, head_dim=128,
+             block_size=16, num_blocks=64, max_blocks_per_seq=8, max_seq_len=100,
+             kv_dtype=kb.KVD_KV_BF16, k_cache=FAKE, v_cache=FAKE + 0x10000, block_table=FAKE + 0x20000,
+             seq_lens=FAKE + 0x30000)
+    d.update(kw)
+    return kb.KvdPagedKV(**d)
+
+
+BAD = [
+    (dict(num_seqs=-1), kb.KVD_ERR_SHAPE),
+    (dict(q_tokens_per_seq=0), kb.KVD_ERR_SHAPE),
+    (dict(q_tokens_per_seq=17), kb.KVD_ERR_UNSUPPORTED),
+    (dict(n_q_heads=6, n_kv_heads=4), kb.KVD_ERR_SHAPE),
+    (dict(n_kv_heads=0), kb.KVD_ERR_SHAPE),
+    (dict(head_dim=96), kb.KVD_ERR_UNSUPPORTED),
+    (dict(head_dim=8), kb.KVD_ERR_UNSUPPORTED),
+    (dict(block_size=0), kb.KVD_ERR_UNSUPPORTED),
+    (dict(block_size=24), kb.KVD_ERR_UNSUPPORTED),
+    (dict(block_size=2048), kb.KVD_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), kb.KVD_ERR_SHAPE),
+    (dict(max_seq_len=0), kb.KVD_ERR_SHAPE),
+    (dict(q_tokens_per_seq=4, max_seq_len=3), kb.KVD_ERR_SHAPE),
+    (dict(max_seq_len=129), kb.KVD_ERR_SHAPE),            # > 8 blocks * 16
+    (dict(kv_dtype=2), kb.KVD_ERR_UNSUPPORTED),
+    (dict(k_cache=0), kb.KVD_ERR_NULL),
+    (dict(block_table=0), kb.KVD_ERR_NULL),
+    (dict(seq_lens=0), kb.KVD_ERR_NULL),
+    (dict(k_cache=FAKE + 8), kb.KVD_ERR_SHAPE),           # misaligned
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD, ids=[str(k) for k, _ in BAD])
+def test_bad_descriptor_rejected_before_launch(kw, status):
+    d = desc(**kw)
+    L = kb.lib()
+    ws = ctypes.c_void_p(FAKE)
+    st = L.kvd_decode_attention(ctypes.byref(d), FAKE, FAKE, 0.0, ws, 1 << 30, None)
+    assert st == status, kb.last_error()
+    assert kb.last_error()
+    st = L.kvd_rope_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 10000.0, 0, None)
+    assert st == status, kb.last_error()
+    assert L.kvd_decode_attention_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
+
+
+def test_null_descriptor():
+    L = kb.lib()
+    assert L.kvd_decode_attention(None, FAKE, FAKE, 0.0, None, 0, None) == kb.KVD_ERR_NULL
+    assert L.kvd_rope_append_kv(None, FAKE, FAKE, FAKE, FAKE, 1e4, 0, None) == kb.KVD_ERR_NULL
+
+
+def test_bad_call_arguments():
+    L = kb.lib()
+    d = desc(max_blocks_per_seq=64, max_seq_len=1000)
+    assert L.kvd_rope_append_kv(ctypes.byref(d), 0, FAKE, FAKE, FAKE, 1e4, 0, None) == kb.KVD_ERR_NULL
+    assert L.kvd_rope_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -1.0, 0, None) == kb.KVD_ERR_SHAPE
+    assert L.kvd_rope_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, float("inf"), 0, None) == kb.KVD_ERR_SHAPE
+    assert L.kvd_rope_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1e4, 2, None) == kb.KVD_ERR_UNSUPPORTED
+    assert L.kvd_decode_attention(ctypes.byref(d), 0, FAKE, 0.0, None, 0, None) == kb.KVD_ERR_NULL
+    assert L.kvd_decode_attention(ctypes.byref(d), FAKE, FAKE, float("nan"), None, 0, None) == kb.KVD_ERR_SHAPE
+    need = L.kvd_decode_attention_workspace_size(ctypes.byref(d))
+    assert need > 0
+    assert L.kvd_decode_attention(ctypes.byref(d), FAKE, FAKE, 0.0, None, 0, None) == kb.KVD_ERR_WORKSPACE
+    assert L.kvd_decode_attention(ctypes.byref(d), FAKE, FAKE, 0.0, FAKE, need - 1, None) == kb.KVD_ERR_WORKSPACE
+    assert L.kvd_decode_attention(ctypes.byref(d), FAKE, FAKE, 0.0, FAKE + 16, need, None) == kb.KVD_ERR_WORKSPACE
+    bad_kernel = kb.KvdAttnOptions(0, 7)
+    assert L.kvd_decode_attention_ex(ctypes.byref(d), FAKE, FAKE, 0.0, ctypes.byref(bad_kernel), FAKE,
+                                     need, None) == kb.KVD_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_noop():
+    L = kb.lib()
+    d = desc(num_seqs=0, k_cache=0, v_cache=0, block_table=0, seq_lens=0)
+    assert L.kvd_decode_attention(ctypes.byref(d), 0, 0, 0.0, None, 0, None) == kb.KVD_OK
+    assert L.kvd_rope_append_kv(ctypes.byref(d), 0, 0, 0, 0, 1e4, 0, None) == kb.KVD_OK
+    assert L.kvd_decode_attention_workspace_size(ctypes.byref(d)) == 0
+
+
+def _plan(d, splits=0, kernel=0):
+    s, k, kern = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    o = kb.KvdAttnOptions(splits, kernel)
+    st = kb.lib().kvd_decode_attention_plan(ctypes.byref(d), ctypes.byref(o), ctypes.byref(s),
+                                            ctypes.byref(k), ctypes.byref(kern))
+    assert st == 0, kb.last_error()
+    return s.value, k.value, kern.value
+
+
+@pytest.mark.parametrize("max_len", [1, 2, 17, 255, 256, 257, 4097, 8193, 16388, 131073])
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 1, 4, 4), (16, 1, 32, 8), (64, 1, 16, 8), (4, 1, 64, 8),
+                                        (32, 4, 32, 8)])
+def test_plan_covers_every_key(max_len, B, T, Hq, Hkv):
+    if max_len < T:
+        return
+    bs = 16
+    d = desc(num_seqs=B, q_tokens_per_seq=T, n_q_heads=Hq, n_kv_heads=Hkv,
+             max_blocks_per_seq=(max_len + bs - 1) // bs, max_seq_len=max_len)
+    for forced in (0, 1, 3, 1000):
+        s, k, _ = _plan(d, forced)
+        assert s >= 1 and k >= 1
+        assert s * k >= max_len, "splits must cover every key"
+        assert (s - 1) * k < max_len, "no split may start past the longest sequence"
+        if forced:
+            assert s <= forced
+        ws = kb.lib().kvd_decode_attention_workspace_size_ex(ctypes.byref(d),
+                                                             ctypes.byref(kb.KvdAttnOptions(forced, 0)))
+        rows = B * T * Hq
+        if s == 1:
+            assert ws == 0
+        else:
+            assert ws >= rows * s * (128 + 2) * 4

@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+* The append is bit-exact: the whole K and V pools after the step equal the
+  oracle's, bit for bit (the poisoned tail slots and spare blocks included).
+* q_rot is the fp64 rotation rounded once to fp32.
+* Attention: fp32 caches within 1e-5 max-abs, bf16 caches (fp32 accumulate)
+  within 2e-3 normwise relative (max|gpu - ref| / max|ref|).
+Small variants of the five configurations are checked on every row; the full
+configurations run in the launch configuration the benchmark times and are
+checked on sampled rows (every sequence's first and last row included).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from full_recompute import recompute_last_rows
+from gpu_common import (GpuCase, assert_parity, assert_qrot, cached_workload, note, oracle_step,
+                        rel_err)
+from helpers import oracle_cache
+from kv_cached_decode_amd import binding as kb
+from kv_cached_decode_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+
+SMALL = [workloads.small_variant(n) for n in workloads.CONFIG_ORDER[1:]]
+FULL = [workloads.CONFIGS[n] for n in workloads.CONFIG_ORDER[1:]]
+
+
+@needs_gpu
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_small_configs_all_rows(spec):
+    w = cached_workload(spec)
+    note("small", spec.name)
+    case = GpuCase(w)
+    q_gpu, out_gpu = case.step()
+    kp, vp = case.pools()
+    q_ref, out_ref, kp_ref, vp_ref = oracle_step(w)
+    assert np.array_equal(kp, kp_ref), "K pool differs from the oracle's after the append"
+    assert np.array_equal(vp, vp_ref), "V pool differs from the oracle's after the append"
+    assert_qrot(q_gpu, q_ref)
+    e = assert_parity(spec, out_gpu, out_ref)
+    print(f"{spec.name}: error {e:.3e}")
+
+
+@needs_gpu
+@pytest.mark.parametrize("spec", FULL, ids=lambda s: s.name)
+def test_full_configs_sampled_rows(spec):
+    w = cached_workload(spec)
+    rows = workloads.sample_rows(spec, 96, seed=1)
+    note("full", spec.name, "rows", rows.size, "plan", )
+    case = GpuCase(w)
+    note("plan", kb.decode_attention_plan(case.kv))
+    q_gpu, out_gpu = case.step()
+    kp, vp = case.pools()
+    q_ref, out_ref, kp_ref, vp_ref = oracle_step(w, rows=rows)
+    assert np.array_equal(kp, kp_ref), "K pool differs from the oracle's after the append"
+    assert np.array_equal(vp, vp_ref), "V pool differs from the oracle's after the append"
+    assert_qrot(q_gpu, q_ref)
+    got = out_gpu.reshape(-1, spec.head_dim)[rows]
+    e = assert_parity(spec, got, out_ref)
+    print(f"{spec.name}: error {e:.3e} on {rows.size} rows")
+
+
+@needs_gpu
+def test_tiny_config_append_chain():
+    """Tiny fp32 configuration: 32 GPU appends at positions 0..31, then the
+    decode step at position 32; pools and output against the oracle's chain and
+    the output against the full non-cached recompute."""
+    w = workloads.make_workload(workloads.CONFIGS["tiny_f32"])
+    s = w.spec
+    note("tiny chain")
+    case = GpuCase(w)
+    oc_k, oc_v = w.k_pool.copy(), w.v_pool.copy()
+    for p in range(33):
+        sl = np.array([p + 1], np.int32)
+        case.seq_lens.copy_(torch.from_numpy(sl))
+        case.kv.max_seq_len = p + 1
+        case.q.copy_(torch.from_numpy(np.ascontiguousarray(w.prefix_q[:, p:p + 1])))
+        case.k.copy_(torch.from_numpy(np.ascontiguousarray(w.prefix_k[:, p:p + 1])))
+        case.v.copy_(torch.from_numpy(np.ascontiguousarray(w.prefix_v[:, p:p + 1])))
+        q_gpu, out_gpu = case.step()
+        oc = oracle_cache(w, seq_lens=sl, k_pool=oc_k, v_pool=oc_v)
+        q_ref = oc.rope_append_kv(np.ascontiguousarray(w.prefix_q[:, p:p + 1]),
+                                  np.ascontiguousarray(w.prefix_k[:, p:p + 1]),
+                                  np.ascontiguousarray(w.prefix_v[:, p:p + 1]), s.rope_base)
+        out_ref = oc.decode_attention(q_ref)
+        oc_k, oc_v = oc.k_pool, oc.v_pool
+        kp, vp = case.pools()
+        assert np.array_equal(kp.view(np.uint32), oc_k.view(np.uint32)), p
+        assert np.array_equal(vp.view(np.uint32), oc_v.view(np.uint32)), p
+        assert_parity(s, out_gpu, out_ref)
+    store = lambda a: a.astype(np.float32).astype(np.float64)  # noqa: E731
+    ref, _ = recompute_last_rows(w.prefix_q[0], w.prefix_k[0], w.prefix_v[0], 1, s.rope_base,
+                                 s.layout, store)
+    assert np.max(np.abs(out_gpu[0] - ref)) <= 1e-5
+
+
+@needs_gpu
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 1000])
+def test_split_count_does_not_change_the_result(splits):
+    spec = workloads.small_variant("llama3_8b")
+    w = cached_workload(spec)
+    note("splits", splits)
+    case = GpuCase(w)
+    _, out_auto = case.step()
+    q_rot = kb.rope_append_kv(case.kv, case.q, case.k, case.v, rope_base=spec.rope_base)
+    out = case.attention(q_rot, num_splits=splits)
+    again = case.attention(q_rot, num_splits=splits)
+    assert np.array_equal(out, again), "not deterministic for a fixed plan"
+    q_ref, out_ref, _, _ = oracle_step(w)
+    assert_parity(spec, out, out_ref)
+    assert rel_err(out, out_auto) < 1e-5
+
+
+EDGE = [
+    # name, B, T, Hq, Hkv, D, bs, dtype, ctx, layout
+    ("single_key", 3, 1, 8, 2, 128, 16, "bf16", 0, 0),
+    ("draft_only", 2, 4, 8, 2, 128, 16, "bf16", 0, 0),
+    ("block_size_1", 2, 1, 4, 2, 64, 1, "bf16", (1, 300), 0),
+    ("block_size_1024", 2, 2, 4, 1, 128, 1024, "bf16", (1000, 3000), 0),
+    ("d16_bf16", 2, 1, 4, 4, 16, 16, "bf16", (5, 900), 1),
+    ("d32_f32", 2, 1, 4, 2, 32, 8, "f32", (5, 900), 0),
+    ("d64_f32", 3, 2, 6, 3, 64, 32, "f32", (5, 700), 1),
+    ("d128_f32", 2, 1, 8, 2, 128, 16, "f32", (100, 1500), 0),
+    ("d256_bf16", 2, 1, 4, 2, 256, 16, "bf16", (100, 1500), 0),
+    ("d256_f32", 2, 3, 4, 2, 256, 16, "f32", (10, 600), 0),
+    ("many_rows_g16", 2, 1, 32, 2, 128, 16, "bf16", (10, 2000), 0),
+    ("verify_t8", 2, 8, 8, 4, 128, 16, "bf16", (0, 900), 0),
+    ("verify_t16_f32", 1, 16, 4, 4, 64, 16, "f32", 333, 1),
+    ("interleaved", 3, 1, 8, 8, 128, 64, "bf16", (1, 2000), 1),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("case_", EDGE, ids=lambda c: c[0])
+def test_edge_cases(case_):
+    name, B, T, Hq, Hkv, D, bs, dtype, ctx, layout = case_
+    spec = workloads.Spec(name, B, T, Hq, Hkv, D, bs, dtype, ctx, 10000.0, "normal", "shuffled",
+                          spare_frac=0.2, seed=zlib.crc32(name.encode()) % 1000, layout=layout)
+    w = workloads.make_workload(spec)
+    note("edge", name)
+    case = GpuCase(w)
+    q_gpu, out_gpu = case.step()
+    kp, vp = case.pools()
+    q_ref, out_ref, kp_ref, vp_ref = oracle_step(w)
+    assert np.array_equal(kp.view(np.uint16), kp_ref.view(np.uint16))
+    assert np.array_equal(vp.view(np.uint16), vp_ref.view(np.uint16))
+    assert_qrot(q_gpu, q_ref)
+    assert_parity(spec, out_gpu, out_ref)
+
+
+@needs_gpu
+def test_custom_softmax_scale():
+    spec = workloads.small_variant("qwen3_0_6b_cb")
+    w = cached_workload(spec)
+    note("scale")
+    case = GpuCase(w)
+    _, out = case.step(scale=0.37)
+    _, ref, _, _ = oracle_step(w, scale=0.37)
+    assert_parity(spec, out, ref)
+
+
+@needs_gpu
+def test_empty_batch():
+    note("empty batch")
+    k = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    kv = kb.PagedKV(k, k.clone(), torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                    torch.zeros((0,), dtype=torch.int32, device="cuda"), 4, 1, 1)
+    q = torch.zeros((0, 1, 4, 128), device="cuda")
+    kv_in = torch.zeros((0, 1, 2, 128), device="cuda")
+    kb.rope_append_kv(kv, q, kv_in, kv_in)
+    out = kb.decode_attention(kv, q)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 1, 4, 128)
