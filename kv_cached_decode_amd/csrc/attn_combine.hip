@@ -9,14 +9,34 @@
 // s * split_keys < seq_lens[b]).  Splits whose keys the row cannot see carry
 // l_s = 0 and a very negative m_s, and drop out.
 //
-// One 64-lane workgroup per query row; lanes stride over the head dimension.
 // Fixed summation order, so results are bitwise reproducible.
 #include "kvd_internal.h"
 
 namespace kvd {
 namespace {
 
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+// One workgroup of COMBINE_THREADS per query row.  The split weights
+// 2^(m_s - M) / sum are formed once in LDS (lanes over splits, wave
+// reductions), then each thread owns head-dimension elements and sums its
+// splits with independent loads in flight.
+constexpr int COMBINE_THREADS = 128;
+constexpr int MAX_STAGED_SPLITS = 1024;
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs a) {
+    __shared__ float sm_w[MAX_STAGED_SPLITS];
+    __shared__ float sm_red[2];
     const CacheView& c = a.c;
     const size_t qrow = blockIdx.x;                     // (b*T + t)*Hq + h
     const int b = (int)(qrow / ((size_t)c.T * c.Hq));
@@ -26,14 +46,32 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
     const float* ml = a.part_ml + qrow * S * 2;
     const float* po = a.part_o + qrow * S * c.D;
 
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, ml[2 * s]);
-    float Ls = 0.0f;
-    for (int s = 0; s < n; ++s) Ls += ml[2 * s + 1] * exp2f(ml[2 * s] - M);
-    const float inv = 1.0f / Ls;
-    for (int d = threadIdx.x; d < c.D; d += 64) {
+    if (threadIdx.x < 64) {
+        // wave 0: the max and the weighted sum over splits, 64 at a time
+        float M = -INFINITY;
+        for (int s = threadIdx.x; s < n; s += 64) M = fmaxf(M, ml[2 * s]);
+        M = wave_max(M);
+        float Ls = 0.0f;
+        for (int s = threadIdx.x; s < n; s += 64) {
+            const float w = exp2f(ml[2 * s] - M);
+            Ls += ml[2 * s + 1] * w;
+            if (s < MAX_STAGED_SPLITS) sm_w[s] = w;
+        }
+        Ls = wave_sum(Ls);
+        if (threadIdx.x == 0) {
+            sm_red[0] = M;
+            sm_red[1] = 1.0f / Ls;
+        }
+    }
+    __syncthreads();
+    const float M = sm_red[0], inv = sm_red[1];
+    for (int d = threadIdx.x; d < c.D; d += COMBINE_THREADS) {
         float O = 0.0f;
-        for (int s = 0; s < n; ++s) O += po[(size_t)s * c.D + d] * exp2f(ml[2 * s] - M);
+#pragma unroll 8
+        for (int s = 0; s < n; ++s) {
+            const float w = s < MAX_STAGED_SPLITS ? sm_w[s] : exp2f(ml[2 * s] - M);
+            O += po[(size_t)s * c.D + d] * w;
+        }
         a.out[qrow * c.D + d] = O * inv;
     }
 }
@@ -43,7 +81,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
     const size_t rows = (size_t)a.c.B * a.c.T * a.c.Hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(COMBINE_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -1,10 +1,289 @@
-// attn_mfma.hip -- placeholder until the matrix-core verify kernel lands.
+// attn_mfma.hip -- decode attention on the matrix cores, for multi-token
+// verify (ferrox-models `speculative`: every draft token of a sequence is
+// verified in one batched pass; ferrite's MTP speculation) and any other case
+// where the g*T query rows that share a kv head make Q.K^T a small dense
+// contraction (g*T <= 16 rows, bf16 cache, head_dim 128).
+//
+// Workgroup = 4 wave64s per (split, kv head, sequence), as in the VALU path.
+// Each wave streams 32-key tiles of the workgroup's key range (tiles w, w+4,
+// ... of the range) and keeps its own online-softmax state; the waves merge
+// through LDS at the end.  Per 32-key tile, with M = g*T <= 16 query rows:
+//
+//   S^T[32 keys x 16 rows] = K[32 x 128] . Q^T[128 x 16]
+//       v_mfma_f32_16x16x32_bf16, two 16-key tiles x four 32-dim steps.  The
+//       K operand (lane l: key l%16, 8 consecutive dims) is loaded straight
+//       from the paged cache, 16 keys x 64 contiguous bytes per instruction.
+//       Q is split into bf16 hi + lo parts (q = hi + lo to ~16 bits), so the
+//       scores keep fp32-class accuracy: two MFMAs per step.
+//   softmax: the MFMA result leaves each lane one row (l%16) and 8 keys, so
+//       the row max/sum need only the xor-16/xor-32 lane exchange.
+//   O^T[128 x 16 rows] += V^T[128 x 32] . P^T[32 x 16]
+//       P comes straight out of the score registers (no data movement), again
+//       as bf16 hi + lo.  V^T fragments are read from a row-major LDS copy of
+//       the V tile with ds_read_b64_tr_b16 (each 16-lane group turns 4 key
+//       rows x 16 dims into 16 lanes x 4 keys), two reads per 32-key MFMA.
+//       O^T keeps the row in l%16, so the per-row rescale is lane-local.
+//
+// Keys past the range are clamped to the range's last key for the loads and
+// masked to weight 0; keys past a draft token's position are masked the
+// same way (causal within the draft).
 #include "kvd_internal.h"
 
 namespace kvd {
+namespace {
 
-bool mfma_supported(int, int, int) { return false; }
-int mfma_step_keys() { return 256; }
-hipError_t launch_attn_mfma(const AttnArgs&, hipStream_t) { return hipErrorInvalidValue; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;
+constexpr int D = 128;
+constexpr int TILE = 32;                 // keys per wave iteration
+constexpr int ROWB = D * 2 + 32;         // LDS row stride of the V tile (bytes)
+constexpr int VT_BYTES = TILE * ROWB;    // one wave's V tile
+constexpr float M_EMPTY = -1e30f;
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ inline bf16x8 join(const s16x4& a, const s16x4& b) {
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ inline s16x4 lds_tr(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
+}
+
+__device__ inline float xor_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ inline float xor_sum(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
+    extern __shared__ int sm_blk[];                       // block ids of the key range
+    // the V tiles during the key loop, then the per-wave outputs
+    constexpr int O_BYTES = WAVES * 16 * (D + 1) * 4;
+    static_assert(O_BYTES <= WAVES * VT_BYTES, "output staging must fit in the V tiles");
+    __shared__ __attribute__((aligned(16))) char sm_v[WAVES * VT_BYTES];
+    __shared__ float sm_m[WAVES][16];
+    __shared__ float sm_l[WAVES][16];
+    float (*sm_o)[16][D + 1] = (float (*)[16][D + 1])sm_v;
+
+    const CacheView& c = a.c;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int n16 = lane & 15;          // MFMA column / row-in-tile index
+    const int j = lane >> 4;            // lane group
+
+    const int L = c.seq_lens[b];
+    const int key_begin = split * a.split_keys;
+    if (key_begin >= L) return;
+    const int key_end = min(L, key_begin + a.split_keys);
+
+    const int blk0 = key_begin >> c.log2_bs;
+    const int nblk = ((key_end - 1) >> c.log2_bs) - blk0 + 1;
+    const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
+    for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+
+    // Q^T operand for row n16 (rows >= M are zero): dims 32*kk + 8*j .. +8,
+    // scaled into log2 units and split into bf16 hi + lo.
+    const int row = n16;
+    const bool row_ok = row < a.rows;
+    const int t_row = row_ok ? row / c.g : 0;
+    const int h_row = kvh * c.g + (row_ok ? row - t_row * c.g : 0);
+    const int vis = row_ok ? L - c.T + t_row : L - 1;     // last key this row sees
+    bf16x8 qhi[4], qlo[4];
+    {
+        const float* qp = a.q + (((size_t)b * c.T + t_row) * c.Hq + h_row) * D;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float4 x0 = *(const float4*)(qp + 32 * kk + 8 * j);
+            const float4 x1 = *(const float4*)(qp + 32 * kk + 8 * j + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = row_ok ? xs[e] * a.scale_log2 : 0.0f;
+                const __bf16 hi = (__bf16)v;
+                qhi[kk][e] = hi;
+                qlo[kk][e] = (__bf16)(v - (float)hi);
+            }
+        }
+    }
+    __syncthreads();
+
+    const char* kbase = (const char*)c.k;
+    const char* vbase = (const char*)c.v;
+    const int bs_mask = (1 << c.log2_bs) - 1;
+    char* vt = sm_v + wave * VT_BYTES;
+
+    auto row_addr = [&](const char* base, int key) -> const char* {
+        const int blk = sm_blk[(key >> c.log2_bs) - blk0];
+        const size_t slot = (((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
+        return base + slot * (D * 2);
+    };
+
+    // K operands: tile h (16 keys), step kk: lane l reads key l%16, bytes
+    // [64*kk + 16*j, +16).  V rows: load i reads key 4*i + j, chunk n16.
+    auto issue = [&](int base, u32x4 (&kf)[8], u32x4 (&vf)[8]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const char* kr = row_addr(kbase, min(base + 16 * h + n16, key_end - 1));
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kf[4 * h + kk] = __builtin_nontemporal_load((const u32x4*)(kr + 64 * kk + 16 * j));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const char* vr = row_addr(vbase, min(base + 4 * i + j, key_end - 1));
+            vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
+        }
+    };
+
+    float m = M_EMPTY, lsum = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int base, const u32x4 (&kf)[8], const u32x4 (&vf)[8]) {
+        // V tile -> LDS (row-major, padded rows)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (4 * i + j) * ROWB + 16 * n16) = vf[i];
+
+        // scores: S^T tiles (16 keys x 16 rows) for keys base + 16h + 4j + i
+        f32x4 s[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 kop = as_bf16x8(kf[4 * h + kk]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[kk], acc, 0, 0, 0);
+            }
+            s[h] = acc;
+        }
+        // mask, running max, weights
+        float mx = m;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = base + 16 * h + 4 * j + i;
+                if (key >= key_end || key > vis) s[h][i] = -INFINITY;
+                mx = fmaxf(mx, s[h][i]);
+            }
+        mx = xor_max(mx);
+        const float alpha = fast_exp2(m - mx);
+        m = mx;
+        lsum *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[h][i] - m);
+                lsum += p;
+                const __bf16 hi = (__bf16)p;
+                phi[4 * h + i] = hi;
+                plo[4 * h + i] = (__bf16)(p - (float)hi);
+            }
+        __builtin_amdgcn_wave_barrier();
+        // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i (first half of
+        // the key order) and 16 + 4j + i (second half) of dim tile nt.
+        const char* rd = vt + (4 * j + (n16 >> 2)) * ROWB + 8 * (n16 & 3);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * ROWB + 32 * nt));
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, o[nt], 0, 0, 0);
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, o[nt], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    constexpr int STRIDE = WAVES * TILE;
+    u32x4 kA[8], vA[8], kB[8], vB[8];
+    int base = key_begin + wave * TILE;
+    if (base < key_end) issue(base, kA, vA);
+    while (base < key_end) {
+        int nb = base + STRIDE;
+        if (nb < key_end) issue(nb, kB, vB);
+        compute(base, kA, vA);
+        base = nb;
+        if (base >= key_end) break;
+        nb = base + STRIDE;
+        if (nb < key_end) issue(nb, kA, vA);
+        compute(base, kB, vB);
+        base = nb;
+    }
+
+    // per-wave state -> LDS: row n16's sum over the four lane groups; O^T
+    // element (dim 16*nt + 4*j + i, row n16)
+    lsum = xor_sum(lsum);
+    __syncthreads();          // every wave is done with its V tile
+    if (j == 0) {
+        sm_m[wave][n16] = m;
+        sm_l[wave][n16] = lsum;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_o[wave][n16][16 * nt + 4 * j + i] = o[nt][i];
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
+        const int r = idx / D, d = idx - r * D;
+        if (r >= a.rows) break;
+        float M = sm_m[0][r];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm_m[w][r]);
+        float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float f = fast_exp2(sm_m[w][r] - M);
+            Ls += sm_l[w][r] * f;
+            O += sm_o[w][r][d] * f;
+        }
+        const int t = r / c.g;
+        const int h = kvh * c.g + (r - t * c.g);
+        const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h;
+        if (a.num_splits == 1) {
+            a.out[qrow * D + d] = O / Ls;
+        } else {
+            a.part_o[(qrow * a.num_splits + split) * D + d] = O;
+            if (d == 0) {
+                a.part_ml[(qrow * a.num_splits + split) * 2 + 0] = M;
+                a.part_ml[(qrow * a.num_splits + split) * 2 + 1] = Ls;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool mfma_supported(int D_, int kv_bf16, int rows) { return D_ == D && kv_bf16 && rows >= 1 && rows <= 16; }
+
+int mfma_step_keys() { return WAVES * TILE; }
+
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
+    const size_t lds = sizeof(int) * (size_t)(((a.split_keys - 1) >> a.c.log2_bs) + 2);
+    dim3 grid(a.num_splits, a.c.Hkv, a.c.B);
+    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), lds, s, a);
+    return hipGetLastError();
+}
 
 }  // namespace kvd

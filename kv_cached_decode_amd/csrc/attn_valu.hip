@@ -23,24 +23,27 @@
 //        them, bitwise identical.
 //   softmax: online, in log2 units (scale*log2(e) folded into q).  Each lane
 //        group keeps its own running max m, sum l and output o for the keys it
-//        has seen; m is only raised when a score exceeds it by more than TAU
-//        (2^TAU headroom in fp32), so the rescale branch is rare.
+//        has seen, rescaled once per step (not per key).
 //   PV:  the V registers are in the same lane layout, so o += p * v needs no
 //        data movement.
+//   memory: the block ids of the workgroup's key range are staged in LDS
+//        once; the K/V loads of the next step are issued before the current
+//        step is computed (two register buffers), so each wave keeps a step's
+//        rows in flight while it computes.
 //   merge: groups of a wave merge by shuffles, the four waves through LDS;
 //        the workgroup writes either the final row (one split) or its
 //        unnormalised partial (m, l, o) for the combine kernel.
 //
-// Keys past the sequence end are never loaded (their slots may hold NaN);
-// keys past a draft token's own position get score -inf and weight 0.
+// Keys past the sequence end are never loaded (their slots may hold NaN):
+// lanes past the range re-load the range's last key and weight it 0; keys past
+// a draft token's own position get score -inf and weight 0.
 #include "kvd_internal.h"
 
 namespace kvd {
 namespace {
 
 constexpr int WAVES = 4;
-constexpr int U = 8;              // groups per wave per step
-constexpr float TAU = 8.0f;       // lazy-rescale headroom, log2 units
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte load
 constexpr float M_EMPTY = -1e30f; // running max before any key is seen
 
 template <int CTRL>
@@ -61,8 +64,10 @@ __device__ inline float group_sum(float x) {
     return x;
 }
 
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int KV, int EPL>
-__device__ inline void to_f32(const uint4& r, float (&f)[EPL]) {
+__device__ inline void to_f32(const u32x4& r, float (&f)[EPL]) {
     if constexpr (KV) {
         const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -78,15 +83,24 @@ __device__ inline void to_f32(const uint4& r, float (&f)[EPL]) {
     }
 }
 
+// Keys per wave step for a head_dim / cache type.
+template <int D, int KV>
+struct Geo {
+    static constexpr int ESZ = KV ? 2 : 4;
+    static constexpr int EPL = 16 / ESZ;     // elements per lane per key
+    static constexpr int LPK = D / EPL;      // lanes per key
+    static constexpr int KPG = 64 / LPK;     // keys per group (one dwordx4 per lane)
+    static constexpr int U = KPG >= 8 ? 2 : 4;   // groups per wave step
+    static constexpr int WAVE_KEYS = U * KPG;
+};
+
 template <int D, int KV, int RT>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
-    constexpr int ESZ = KV ? 2 : 4;
-    constexpr int EPL = 16 / ESZ;        // elements per lane per key
-    constexpr int LPK = D / EPL;         // lanes per key
-    constexpr int KPG = 64 / LPK;        // keys per group
-    constexpr int WAVE_KEYS = U * KPG;
+    using G = Geo<D, KV>;
+    constexpr int EPL = G::EPL, LPK = G::LPK, KPG = G::KPG, U = G::U, WAVE_KEYS = G::WAVE_KEYS;
     static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "unsupported head_dim");
 
+    extern __shared__ int sm_blk[];              // block ids of this split's key range
     __shared__ float sm_o[WAVES][RT][D];
     __shared__ float sm_m[WAVES][RT];
     __shared__ float sm_l[WAVES][RT];
@@ -104,6 +118,12 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     if (key_begin >= L) return;               // empty split: the combine skips it
     const int key_end = min(L, key_begin + a.split_keys);
 
+    // stage the block ids of [key_begin, key_end) in LDS
+    const int blk0 = key_begin >> c.log2_bs;
+    const int nblk = ((key_end - 1) >> c.log2_bs) - blk0 + 1;
+    const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
+    for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+
     const int kslot = lane / LPK;
     const int chunk = lane % LPK;
     const int row0 = rtile * RT;
@@ -118,9 +138,15 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         const int t = ok ? row / c.g : 0;
         const int h = kvh * c.g + (ok ? row - t * c.g : 0);
         vis[r] = ok ? L - c.T + t : -1;       // last visible key (inclusive)
-        const float* qp = a.q + (((size_t)b * c.T + t) * c.Hq + h) * D + chunk * EPL;
+        const float4* qp = (const float4*)(a.q + (((size_t)b * c.T + t) * c.Hq + h) * D + chunk * EPL);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[r][e] = ok ? qp[e] * a.scale_log2 : 0.0f;
+        for (int e4 = 0; e4 < EPL / 4; ++e4) {
+            const float4 v = qp[e4];
+            qv[r][4 * e4 + 0] = ok ? v.x * a.scale_log2 : 0.0f;
+            qv[r][4 * e4 + 1] = ok ? v.y * a.scale_log2 : 0.0f;
+            qv[r][4 * e4 + 2] = ok ? v.z * a.scale_log2 : 0.0f;
+            qv[r][4 * e4 + 3] = ok ? v.w * a.scale_log2 : 0.0f;
+        }
     }
 
     float m[RT], l[RT], o[RT][EPL];
@@ -131,63 +157,86 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[r][e] = 0.0f;
     }
+    __syncthreads();
 
     const char* kbase = (const char*)c.k;
     const char* vbase = (const char*)c.v;
-    const int* trow = c.table + (size_t)b * c.max_blocks;
     const int bs_mask = (1 << c.log2_bs) - 1;
-    const size_t row_bytes = (size_t)D * ESZ;
+    constexpr size_t ROW_BYTES = (size_t)D * G::ESZ;
 
-    for (int base = key_begin + wave * WAVE_KEYS; base < key_end; base += WAVES * WAVE_KEYS) {
-        uint4 kr[U], vr[U];
+    // Issue the loads of one wave step.  Keys past the range are clamped to
+    // the last key of the range (finite data; masked to weight 0 below), so
+    // the loads need no branch.
+    auto issue = [&](int base, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = base + u * KPG + kslot;
-            if (j < key_end) {
-                const int blk = trow[j >> c.log2_bs];
-                const size_t slot = ((((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (j & bs_mask));
-                const size_t off = slot * row_bytes + (size_t)chunk * 16;
-                kr[u] = *(const uint4*)(kbase + off);
-                vr[u] = *(const uint4*)(vbase + off);
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
-            }
+            const int j = min(base + u * KPG + kslot, key_end - 1);
+            const int blk = sm_blk[(j >> c.log2_bs) - blk0];
+            const size_t slot = (((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (j & bs_mask);
+            const size_t off = slot * ROW_BYTES + (size_t)chunk * 16;
+            kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
+            vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
         }
+    };
+
+    auto compute = [&](int base, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
+        float s[U][RT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + u * KPG + kslot;
             float kf[EPL];
             to_f32<KV, EPL>(kr[u], kf);
-            float s[RT];
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 float acc = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc += qv[r][e] * kf[e];
-                s[r] = group_sum<LPK>(acc);
-                if (j >= key_end || j > vis[r]) s[r] = -INFINITY;
+                acc = group_sum<LPK>(acc);
+                s[u][r] = (j >= key_end || j > vis[r]) ? -INFINITY : acc;
             }
+        }
+        // one rescale per step and row
 #pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                if (s[r] > m[r] + TAU) {              // rare: raise the running max
-                    const float alpha = exp2f(m[r] - s[r]);
-                    l[r] *= alpha;
+        for (int r = 0; r < RT; ++r) {
+            float mx = m[r];
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
-                    m[r] = s[r];
-                }
-            }
+            for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][r]);
+            const float alpha = fast_exp2(m[r] - mx);
+            m[r] = mx;
+            l[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             float vf[EPL];
             to_f32<KV, EPL>(vr[u], vf);
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const float p = exp2f(s[r] - m[r]);
+                const float p = fast_exp2(s[u][r] - m[r]);
                 l[r] += p;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) o[r][e] += p * vf[e];
             }
         }
+    };
+
+    // software pipeline: the next step's loads are in flight while this one
+    // is computed
+    constexpr int STRIDE = WAVES * WAVE_KEYS;
+    u32x4 kA[U], vA[U], kB[U], vB[U];
+    int base = key_begin + wave * WAVE_KEYS;
+    if (base < key_end) issue(base, kA, vA);
+    while (base < key_end) {
+        int nb = base + STRIDE;
+        if (nb < key_end) issue(nb, kB, vB);
+        compute(base, kA, vA);
+        base = nb;
+        if (base >= key_end) break;
+        nb = base + STRIDE;
+        if (nb < key_end) issue(nb, kA, vA);
+        compute(base, kB, vB);
+        base = nb;
     }
 
     // merge the KPG key groups of this wave (lanes chunk + LPK*kslot)
@@ -198,7 +247,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
             const float mo = __shfl_xor(m[r], off);
             const float lo = __shfl_xor(l[r], off);
             const float mn = fmaxf(m[r], mo);
-            const float as = exp2f(m[r] - mn), bs = exp2f(mo - mn);
+            const float as = fast_exp2(m[r] - mn), bs = fast_exp2(mo - mn);
             l[r] = l[r] * as + lo * bs;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
@@ -232,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         float Ls = 0.0f, O = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const float f = exp2f(sm_m[w][r] - M);
+            const float f = fast_exp2(sm_m[w][r] - M);
             Ls += sm_l[w][r] * f;
             O += sm_o[w][r][d] * f;
         }
@@ -253,11 +302,13 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 
 template <int D, int KV>
 hipError_t launch_rt(const AttnArgs& a, dim3 grid, hipStream_t s) {
+    // block ids of one split's key range: it spans at most this many blocks
+    const size_t lds = sizeof(int) * (size_t)(((a.split_keys - 1) >> a.c.log2_bs) + 2);
     switch (a.row_tile) {
-        case 1: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 4>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 8>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 1>), grid, dim3(256), lds, s, a); break;
+        case 2: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 2>), grid, dim3(256), lds, s, a); break;
+        case 4: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 4>), grid, dim3(256), lds, s, a); break;
+        case 8: hipLaunchKernelGGL((attn_valu_kernel<D, KV, 8>), grid, dim3(256), lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -278,11 +329,26 @@ hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 int valu_step_keys(int D, int kv_bf16) {
-    const int lpk = D / (kv_bf16 ? 8 : 4);
-    return WAVES * U * (64 / lpk);
+    int wk = 0;
+    switch (D * 2 + kv_bf16) {
+        case 32: wk = Geo<16, 0>::WAVE_KEYS; break;
+        case 33: wk = Geo<16, 1>::WAVE_KEYS; break;
+        case 64: wk = Geo<32, 0>::WAVE_KEYS; break;
+        case 65: wk = Geo<32, 1>::WAVE_KEYS; break;
+        case 128: wk = Geo<64, 0>::WAVE_KEYS; break;
+        case 129: wk = Geo<64, 1>::WAVE_KEYS; break;
+        case 256: wk = Geo<128, 0>::WAVE_KEYS; break;
+        case 257: wk = Geo<128, 1>::WAVE_KEYS; break;
+        case 512: wk = Geo<256, 0>::WAVE_KEYS; break;
+        case 513: wk = Geo<256, 1>::WAVE_KEYS; break;
+        default: return 256;
+    }
+    return WAVES * wk;
 }
 
 int valu_max_row_tile(int, int) { return 8; }
+
+int valu_max_split_keys(int log2_bs) { return (VALU_MAX_STAGED_BLOCKS - 2) << log2_bs; }
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s) {
     const int n_rtiles = (a.rows + a.row_tile - 1) / a.row_tile;

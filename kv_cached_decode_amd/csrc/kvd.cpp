@@ -142,11 +142,13 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     p->kernel = kernel;
 
     int step, n_rtiles;
+    int64_t max_keys = INT32_MAX;
     if (kernel == KVD_KERNEL_MFMA) {
         step = kvd::mfma_step_keys();
         p->row_tile = 16;
         n_rtiles = 1;
     } else {
+        max_keys = kvd::valu_max_split_keys(ilog2(kv->block_size));
         step = kvd::valu_step_keys(D, bf16);
         const int max_rt = kvd::valu_max_row_tile(D, bf16);
         int rt = 1;
@@ -168,6 +170,7 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
         if (splits < 1) splits = 1;
     }
     splits = std::min<int64_t>(splits, max_splits);
+    splits = std::max<int64_t>(splits, cdiv(max_len, max_keys));   // per-split staging limit
     if (splits < 1) splits = 1;
     int64_t keys = cdiv(cdiv(max_len, splits), step) * step;
     splits = cdiv(max_len, keys);

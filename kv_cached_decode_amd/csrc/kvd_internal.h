@@ -54,6 +54,9 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
 // Kernel-family properties the planner needs.
 int valu_step_keys(int D, int kv_bf16);      // keys per workgroup step
 int valu_max_row_tile(int D, int kv_bf16);   // rows one workgroup can hold
+// Block ids of one split are staged in LDS; this bounds keys per split.
+constexpr int VALU_MAX_STAGED_BLOCKS = 4096;
+int valu_max_split_keys(int log2_bs);
 bool mfma_supported(int D, int kv_bf16, int rows);
 int mfma_step_keys();
 

@@ -8,8 +8,8 @@
 // evaluated once per token in fp64 and shared through LDS; every head's pair
 // is then rotated in fp64 and rounded once: to fp32 for q_rot and an fp32
 // cache, to bf16 (round to nearest even) for a bf16 cache.  The volume is
-// tiny (B*T*(Hq + 2*Hkv)*D elements), so the kernel is latency-bound and is
-// kept simple: coalesced loads and stores along the head dimension.
+// tiny (B*T*(Hq + 2*Hkv)*D elements), so the kernel is latency-bound: it
+// spreads a token's heads over several workgroups, one pair per thread.
 #include "bf16_round.h"
 #include "kvd_internal.h"
 
@@ -27,6 +27,10 @@ __device__ inline void rotate(double x, double y, double c, double s, double& xr
     yr = x * s + y * c;
 }
 
+// Heads of one token are numbered q heads, then k heads, then v heads; a
+// workgroup rotates/stores HEADS_PER_WG of them (D/2 pair slots each), so
+// every thread touches one pair with no loop and the token's loads and stores
+// are all in flight together.
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     __shared__ double cs[128];
     __shared__ double sn[128];
@@ -44,48 +48,57 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     }
     __syncthreads();
 
-    // queries -> q_rot (fp32); q and q_rot may alias: each pair is read and
-    // written by the same thread.
-    const float* q = a.q + (size_t)token * c.Hq * D;
-    float* qr = a.q_rot + (size_t)token * c.Hq * D;
-    for (int w = threadIdx.x; w < c.Hq * half; w += blockDim.x) {
-        int h = w / half, i = w - h * half, ia, ic;
-        pair_of(i, half, a.interleaved, ia, ic);
-        double xr, yr;
-        rotate(q[h * D + ia], q[h * D + ic], cs[i], sn[i], xr, yr);
-        qr[h * D + ia] = (float)xr;
-        qr[h * D + ic] = (float)yr;
-    }
+    const int heads_per_wg = blockDim.x / half;
+    const int head = blockIdx.y * heads_per_wg + (int)threadIdx.x / half;
+    const int i = (int)threadIdx.x % half;
+    if ((int)threadIdx.x >= heads_per_wg * half || head >= c.Hq + 2 * c.Hkv) return;
 
+    int ia, ic;
+    pair_of(i, half, a.interleaved, ia, ic);
+    if (head < c.Hq) {
+        // query -> q_rot (fp32); q and q_rot may alias: the pair is read and
+        // written by this thread only.
+        const size_t o = ((size_t)token * c.Hq + head) * D;
+        double xr, yr;
+        rotate(a.q[o + ia], a.q[o + ic], cs[i], sn[i], xr, yr);
+        a.q_rot[o + ia] = (float)xr;
+        a.q_rot[o + ic] = (float)yr;
+        return;
+    }
     // the cache slot of this token
     const int blk = c.table[(size_t)b * c.max_blocks + (pos >> c.log2_bs)];
     const int off = pos & ((1 << c.log2_bs) - 1);
-    const size_t head_stride = (size_t)D << c.log2_bs;                 // one head of a block
-    const size_t slot = ((size_t)blk * c.Hkv << c.log2_bs) * D + (size_t)off * D;
-    const float* k = a.k + (size_t)token * c.Hkv * D;
-    const float* v = a.v + (size_t)token * c.Hkv * D;
-
-    for (int w = threadIdx.x; w < c.Hkv * half; w += blockDim.x) {
-        int h = w / half, i = w - h * half, ia, ic;
-        pair_of(i, half, a.interleaved, ia, ic);
+    if (head < c.Hq + c.Hkv) {
+        const int h = head - c.Hq;
+        const size_t src = ((size_t)token * c.Hkv + h) * D;
+        const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
         double xr, yr;
-        rotate(k[h * D + ia], k[h * D + ic], cs[i], sn[i], xr, yr);
-        size_t base = slot + h * head_stride;
+        rotate(a.k[src + ia], a.k[src + ic], cs[i], sn[i], xr, yr);
         if (a.kv_bf16) {
             uint16_t* kc = (uint16_t*)c.k;
-            kc[base + ia] = bf16_from_f64(xr);
-            kc[base + ic] = bf16_from_f64(yr);
+            kc[dst + ia] = bf16_from_f64(xr);
+            kc[dst + ic] = bf16_from_f64(yr);
         } else {
             float* kc = (float*)c.k;
-            kc[base + ia] = (float)xr;
-            kc[base + ic] = (float)yr;
+            kc[dst + ia] = (float)xr;
+            kc[dst + ic] = (float)yr;
         }
-    }
-    for (int w = threadIdx.x; w < c.Hkv * D; w += blockDim.x) {
-        int h = w / D, d = w - h * D;
-        size_t idx = slot + h * head_stride + d;
-        if (a.kv_bf16) ((uint16_t*)c.v)[idx] = bf16_from_f32(v[w]);
-        else           ((float*)c.v)[idx] = v[w];
+    } else {
+        const int h = head - c.Hq - c.Hkv;
+        const size_t src = ((size_t)token * c.Hkv + h) * D;
+        const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
+        // two consecutive elements per thread
+        const int d = 2 * i;
+        const float v0 = a.v[src + d], v1 = a.v[src + d + 1];
+        if (a.kv_bf16) {
+            uint16_t* vc = (uint16_t*)c.v;
+            vc[dst + d] = bf16_from_f32(v0);
+            vc[dst + d + 1] = bf16_from_f32(v1);
+        } else {
+            float* vc = (float*)c.v;
+            vc[dst + d] = v0;
+            vc[dst + d + 1] = v1;
+        }
     }
 }
 
@@ -94,7 +107,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
     const int tokens = a.c.B * a.c.T;
     if (tokens == 0) return hipSuccess;
-    hipLaunchKernelGGL(rope_append_kernel, dim3(tokens), dim3(256), 0, s, a);
+    const int half = a.c.D / 2;
+    const int heads_per_wg = 256 / half;
+    const int heads = a.c.Hq + 2 * a.c.Hkv;
+    dim3 grid(tokens, (heads + heads_per_wg - 1) / heads_per_wg);
+    hipLaunchKernelGGL(rope_append_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

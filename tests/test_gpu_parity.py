@@ -176,3 +176,23 @@ def test_empty_batch():
     out = kb.decode_attention(kv, q)
     torch.cuda.synchronize()
     assert out.shape == (0, 1, 4, 128)
+
+
+FAMILY_CASES = [(n, k) for n in ["llama3_8b", "qwen3_0_6b_cb", "long_ctx", "mtp_verify"]
+                for k in (kb.KVD_KERNEL_VALU, kb.KVD_KERNEL_MFMA)]
+
+
+@needs_gpu
+@pytest.mark.parametrize("name,kernel", FAMILY_CASES,
+                         ids=[f"{n}-{'valu' if k == 1 else 'mfma'}" for n, k in FAMILY_CASES])
+def test_each_kernel_family(name, kernel):
+    """Both attention kernels (vector ALU and matrix core) against the oracle
+    on every small configuration, whichever the planner would pick."""
+    spec = workloads.small_variant(name)
+    w = cached_workload(spec)
+    note("family", name, kernel)
+    case = GpuCase(w)
+    _, out = case.step(kernel=kernel)
+    _, ref, _, _ = oracle_step(w)
+    e = assert_parity(spec, out, ref)
+    print(f"{name} kernel {kernel}: error {e:.3e}")
