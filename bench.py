@@ -159,13 +159,18 @@ def cpu_baseline(w, budget_s=12.0):
                       f"query tokens), fp64, OpenMP over query rows; last rep {t_work:.2f} s"}
 
 
-def copy_calibration(dev, nbytes=512 << 20):
-    """Plain device-to-device copies of a known size (for scaling the HBM
-    counters of a profiled run; outside every timed region)."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+CALIB_BYTES = 512 << 20
+
+
+def copy_calibration(dev, nbytes=CALIB_BYTES):
+    """A plain streaming kernel of known traffic (reads nbytes, writes nbytes:
+    torch.neg on fp32), outside every timed region, whose FETCH_SIZE /
+    WRITE_SIZE scale the counters of a profiled run."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
+    torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        torch.neg(a, out=b)
     torch.cuda.synchronize()
 
 

@@ -43,6 +43,8 @@ constexpr int TILE = 32;                 // keys per wave iteration
 constexpr int ROWB = D * 2 + 32;         // LDS row stride of the V tile (bytes)
 constexpr int VT_BYTES = TILE * ROWB;    // one wave's V tile
 constexpr float M_EMPTY = -1e30f;
+constexpr int MAX_PIECE_BLOCKS = 2048;   // block ids staged in LDS at a time
+constexpr int LPT_MAX_SEQS = 256;        // batches ranked longest-first (one rank per thread)
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -69,34 +71,55 @@ __device__ inline float xor_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
-    extern __shared__ int sm_blk[];                       // block ids of the key range
+// Sequence order: workgroups are dispatched in blockIdx order, so sequence
+// slot z of the grid takes the z-th longest sequence (ties by index).  With a
+// ragged batch the longest units start first and the short ones fill the
+// gaps (longest-processing-time-first list scheduling); a uniform batch keeps
+// its natural order.  Computed per workgroup from seq_lens (each thread ranks
+// one sequence against all others), for batches up to LPT_MAX_SEQS; larger
+// batches keep their natural order.
+__device__ inline int lpt_sequence(const CacheView& c, int z, int* sm_len, int* sm_pick) {
+    if (c.B > LPT_MAX_SEQS) return z;
+    for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];
+    __syncthreads();
+    for (int b = threadIdx.x; b < c.B; b += blockDim.x) {
+        const int Lb = sm_len[b];
+        int rank = 0;
+        for (int i = 0; i < c.B; ++i) {
+            const int Li = sm_len[i];
+            rank += (Li > Lb) | ((Li == Lb) & (i < b));
+        }
+        if (rank == z) *sm_pick = b;
+    }
+    __syncthreads();
+    return *sm_pick;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     // the V tiles during the key loop, then the per-wave outputs
     constexpr int O_BYTES = WAVES * 16 * (D + 1) * 4;
     static_assert(O_BYTES <= WAVES * VT_BYTES, "output staging must fit in the V tiles");
     __shared__ __attribute__((aligned(16))) char sm_v[WAVES * VT_BYTES];
+    __shared__ int sm_blk[MAX_PIECE_BLOCKS];
     __shared__ float sm_m[WAVES][16];
     __shared__ float sm_l[WAVES][16];
+    __shared__ int sm_pick;
     float (*sm_o)[16][D + 1] = (float (*)[16][D + 1])sm_v;
 
     const CacheView& c = a.c;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
     const int n16 = lane & 15;          // MFMA column / row-in-tile index
     const int j = lane >> 4;            // lane group
+    const int split = blockIdx.x;
+    const int kvh = blockIdx.y;
+    // the LPT ranking borrows the V-tile LDS (unused until the key loop)
+    const int b = lpt_sequence(c, blockIdx.z, (int*)sm_v, &sm_pick);
 
     const int L = c.seq_lens[b];
     const int key_begin = split * a.split_keys;
-    if (key_begin >= L) return;
+    if (key_begin >= L) return;         // empty split: the combine skips it
     const int key_end = min(L, key_begin + a.split_keys);
-
-    const int blk0 = key_begin >> c.log2_bs;
-    const int nblk = ((key_end - 1) >> c.log2_bs) - blk0 + 1;
-    const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
-    for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
 
     // Q^T operand for row n16 (rows >= M are zero): dims 32*kk + 8*j .. +8,
     // scaled into log2 units and split into bf16 hi + lo.
@@ -122,113 +145,117 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
             }
         }
     }
-    __syncthreads();
 
     const char* kbase = (const char*)c.k;
     const char* vbase = (const char*)c.v;
     const int bs_mask = (1 << c.log2_bs) - 1;
     char* vt = sm_v + wave * VT_BYTES;
 
-    auto row_addr = [&](const char* base, int key) -> const char* {
-        const int blk = sm_blk[(key >> c.log2_bs) - blk0];
-        const size_t slot = (((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
-        return base + slot * (D * 2);
-    };
-
-    // K operands: tile h (16 keys), step kk: lane l reads key l%16, bytes
-    // [64*kk + 16*j, +16).  V rows: load i reads key 4*i + j, chunk n16.
-    auto issue = [&](int base, u32x4 (&kf)[8], u32x4 (&vf)[8]) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const char* kr = row_addr(kbase, min(base + 16 * h + n16, key_end - 1));
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                kf[4 * h + kk] = __builtin_nontemporal_load((const u32x4*)(kr + 64 * kk + 16 * j));
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const char* vr = row_addr(vbase, min(base + 4 * i + j, key_end - 1));
-            vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
-        }
-    };
-
     float m = M_EMPTY, lsum = 0.0f;
     f32x4 o[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](int base, const u32x4 (&kf)[8], const u32x4 (&vf)[8]) {
-        // V tile -> LDS (row-major, padded rows)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (4 * i + j) * ROWB + 16 * n16) = vf[i];
+    // pieces of at most MAX_PIECE_BLOCKS cache blocks (block ids in LDS)
+    for (int p0 = key_begin; p0 < key_end;) {
+        const int blk0 = p0 >> c.log2_bs;
+        const int p1 = (int)min((long long)key_end, ((long long)blk0 + MAX_PIECE_BLOCKS) << c.log2_bs);
+        const int nblk = ((p1 - 1) >> c.log2_bs) - blk0 + 1;
+        const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
+        __syncthreads();                      // the previous piece (or the ranking) is done with LDS
+        for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+        __syncthreads();
 
-        // scores: S^T tiles (16 keys x 16 rows) for keys base + 16h + 4j + i
-        f32x4 s[2];
+        auto row_addr = [&](const char* base, int key) -> const char* {
+            const int blk = sm_blk[(key >> c.log2_bs) - blk0];
+            const size_t slot = (((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
+            return base + slot * (D * 2);
+        };
+        // K operands: tile h (16 keys), step kk: lane l reads key l%16,
+        // bytes [64*kk + 16*j, +16).  V rows: load i reads key 4*i + j, chunk
+        // n16.  Keys past the piece re-read its last key (weight 0 below).
+        auto issue = [&](int base, u32x4 (&kf)[8], u32x4 (&vf)[8]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int h = 0; h < 2; ++h) {
+                const char* kr = row_addr(kbase, min(base + 16 * h + n16, p1 - 1));
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 kop = as_bf16x8(kf[4 * h + kk]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[kk], acc, 0, 0, 0);
+                for (int kk = 0; kk < 4; ++kk)
+                    kf[4 * h + kk] = __builtin_nontemporal_load((const u32x4*)(kr + 64 * kk + 16 * j));
             }
-            s[h] = acc;
-        }
-        // mask, running max, weights
-        float mx = m;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = base + 16 * h + 4 * j + i;
-                if (key >= key_end || key > vis) s[h][i] = -INFINITY;
-                mx = fmaxf(mx, s[h][i]);
+            for (int i = 0; i < 8; ++i) {
+                const char* vr = row_addr(vbase, min(base + 4 * i + j, p1 - 1));
+                vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
             }
-        mx = xor_max(mx);
-        const float alpha = fast_exp2(m - mx);
-        m = mx;
-        lsum *= alpha;
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
-        bf16x8 phi, plo;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[h][i] - m);
-                lsum += p;
-                const __bf16 hi = (__bf16)p;
-                phi[4 * h + i] = hi;
-                plo[4 * h + i] = (__bf16)(p - (float)hi);
-            }
-        __builtin_amdgcn_wave_barrier();
-        // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i (first half of
-        // the key order) and 16 + 4j + i (second half) of dim tile nt.
-        const char* rd = vt + (4 * j + (n16 >> 2)) * ROWB + 8 * (n16 & 3);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * ROWB + 32 * nt));
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, o[nt], 0, 0, 0);
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, o[nt], 0, 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
-    };
+        };
 
-    constexpr int STRIDE = WAVES * TILE;
-    u32x4 kA[8], vA[8], kB[8], vB[8];
-    int base = key_begin + wave * TILE;
-    if (base < key_end) issue(base, kA, vA);
-    while (base < key_end) {
-        int nb = base + STRIDE;
-        if (nb < key_end) issue(nb, kB, vB);
-        compute(base, kA, vA);
-        base = nb;
-        if (base >= key_end) break;
-        nb = base + STRIDE;
-        if (nb < key_end) issue(nb, kA, vA);
-        compute(base, kB, vB);
-        base = nb;
+        // One buffer of K/V registers per wave: the V rows go to LDS and the
+        // K rows into the score MFMAs first, then the registers take the next
+        // tile's loads, which stay in flight through the softmax and P.V of
+        // this tile (and behind the other wave on the SIMD).
+        u32x4 kf[8], vf[8];
+        constexpr int STRIDE = WAVES * TILE;
+        int base = p0 + wave * TILE;
+        if (base < p1) issue(base, kf, vf);
+        for (; base < p1; base += STRIDE) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (4 * i + j) * ROWB + 16 * n16) = vf[i];
+
+            // scores: S^T tiles (16 keys x 16 rows), keys base + 16h + 4j + i
+            f32x4 s[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x8 kop = as_bf16x8(kf[4 * h + kk]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[kk], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[kk], acc, 0, 0, 0);
+                }
+                s[h] = acc;
+            }
+            if (base + STRIDE < p1) issue(base + STRIDE, kf, vf);
+
+            // mask, running max, weights
+            float mx = m;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = base + 16 * h + 4 * j + i;
+                    if (key >= p1 || key > vis) s[h][i] = -INFINITY;
+                    mx = fmaxf(mx, s[h][i]);
+                }
+            mx = xor_max(mx);
+            const float alpha = fast_exp2(m - mx);
+            m = mx;
+            lsum *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
+            bf16x8 phi, plo;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = fast_exp2(s[h][i] - m);
+                    lsum += p;
+                    const __bf16 hi = (__bf16)p;
+                    phi[4 * h + i] = hi;
+                    plo[4 * h + i] = (__bf16)(p - (float)hi);
+                }
+            __builtin_amdgcn_wave_barrier();
+            // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i (first half
+            // of the key order) and 16 + 4j + i (second half) of dim tile nt.
+            const char* rd = vt + (4 * j + (n16 >> 2)) * ROWB + 8 * (n16 & 3);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * ROWB + 32 * nt));
+                o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, o[nt], 0, 0, 0);
+                o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, o[nt], 0, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        p0 = p1;
     }
 
     // per-wave state -> LDS: row n16's sum over the four lane groups; O^T
@@ -245,6 +272,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) sm_o[wave][n16][16 * nt + 4 * j + i] = o[nt][i];
     __syncthreads();
 
+    // merge the four waves; write the rows (one split) or the partial
     for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
         const int r = idx / D, d = idx - r * D;
         if (r >= a.rows) break;
@@ -280,9 +308,8 @@ bool mfma_supported(int D_, int kv_bf16, int rows) { return D_ == D && kv_bf16 &
 int mfma_step_keys() { return WAVES * TILE; }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-    const size_t lds = sizeof(int) * (size_t)(((a.split_keys - 1) >> a.c.log2_bs) + 2);
     dim3 grid(a.num_splits, a.c.Hkv, a.c.B);
-    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -348,6 +348,38 @@ int valu_step_keys(int D, int kv_bf16) {
 
 int valu_max_row_tile(int, int) { return 8; }
 
+template <int D, int KV>
+static const void* valu_fn(int rt) {
+    switch (rt) {
+        case 1: return (const void*)attn_valu_kernel<D, KV, 1>;
+        case 2: return (const void*)attn_valu_kernel<D, KV, 2>;
+        case 4: return (const void*)attn_valu_kernel<D, KV, 4>;
+        default: return (const void*)attn_valu_kernel<D, KV, 8>;
+    }
+}
+
+int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds) {
+    const void* f = nullptr;
+    switch (D * 2 + kv_bf16) {
+        case 32: f = valu_fn<16, 0>(row_tile); break;
+        case 33: f = valu_fn<16, 1>(row_tile); break;
+        case 64: f = valu_fn<32, 0>(row_tile); break;
+        case 65: f = valu_fn<32, 1>(row_tile); break;
+        case 128: f = valu_fn<64, 0>(row_tile); break;
+        case 129: f = valu_fn<64, 1>(row_tile); break;
+        case 256: f = valu_fn<128, 0>(row_tile); break;
+        case 257: f = valu_fn<128, 1>(row_tile); break;
+        case 512: f = valu_fn<256, 0>(row_tile); break;
+        default: f = valu_fn<256, 1>(row_tile); break;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, dyn_lds) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return 2;
+    }
+    return n;
+}
+
 int valu_max_split_keys(int log2_bs) { return (VALU_MAX_STAGED_BLOCKS - 2) << log2_bs; }
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s) {

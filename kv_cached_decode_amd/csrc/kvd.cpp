@@ -120,10 +120,19 @@ struct Plan {
     int row_tile;
 };
 
-// Split-K plan from host-known sizes only (graph-capture safe).  Aim for a
-// few thousand workgroups so that every CU streams, with at least MIN_STEPS
-// kernel steps of keys per split so the partials stay small next to the
-// cache reads.
+// Split-K plan from host-known sizes only (graph-capture safe).
+//
+// Kernel family: the matrix-core kernel when the g*T query rows sharing a kv
+// head reach MFMA_MIN_ROWS (bf16, head_dim 128), else the vector-ALU kernel.
+// The VALU path spends ~35 VALU instructions per cached key at 4 rows (about
+// 60% VALU-busy at 55-60% of HBM bandwidth); the matrix-core path ~14.
+//
+// Splits: long contiguous ranges stream best.  The matrix-core kernel runs
+// one workgroup per CU when the batch has fewer (sequence, kv head) units
+// than CUs; with more units (continuous batching, ragged lengths) it uses
+// three splits per unit, so the longest-first ordering of the kernel has
+// enough small pieces to balance the CUs.  The VALU kernel targets one round
+// of its resident workgroup slots.
 int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) {
     const int D = kv->head_dim;
     const int bf16 = kv->kv_dtype == KVD_KV_BF16;
@@ -135,39 +144,39 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     const bool mfma_ok = kvd::mfma_supported(D, bf16, p->rows);
     if (kernel == KVD_KERNEL_MFMA && !mfma_ok)
         return fail(KVD_ERR_UNSUPPORTED,
-                    "MFMA kernel needs a bf16 cache, head_dim 128 and g*T <= 16 (rows = %d)",
-                    p->rows);
-    if (kernel == KVD_KERNEL_AUTO) kernel = (mfma_ok && kv->q_tokens_per_seq > 1) ? KVD_KERNEL_MFMA
-                                                                                 : KVD_KERNEL_VALU;
+                    "MFMA kernel needs a bf16 cache, head_dim 128 and g*T <= 16 (rows = %d)", p->rows);
+    if (kernel == KVD_KERNEL_AUTO)
+        kernel = (mfma_ok && p->rows >= kvd::MFMA_MIN_ROWS) ? KVD_KERNEL_MFMA : KVD_KERNEL_VALU;
     p->kernel = kernel;
 
+    const int log2_bs = ilog2(kv->block_size);
+    const int64_t max_len = kv->max_seq_len;
     int step, n_rtiles;
-    int64_t max_keys = INT32_MAX;
+    int64_t max_keys = INT32_MAX, target;
     if (kernel == KVD_KERNEL_MFMA) {
         step = kvd::mfma_step_keys();
         p->row_tile = 16;
         n_rtiles = 1;
+        const int64_t units = (int64_t)kv->num_seqs * kv->n_kv_heads;
+        target = units <= num_cus() ? num_cus() : 3 * units;
     } else {
-        max_keys = kvd::valu_max_split_keys(ilog2(kv->block_size));
+        max_keys = kvd::valu_max_split_keys(log2_bs);
         step = kvd::valu_step_keys(D, bf16);
         const int max_rt = kvd::valu_max_row_tile(D, bf16);
         int rt = 1;
         while (rt < p->rows && rt < max_rt) rt <<= 1;
         p->row_tile = rt;
         n_rtiles = (int)cdiv(p->rows, rt);
+        // about one round of the resident workgroup slots
+        target = (int64_t)kvd::valu_wgs_per_cu(D, bf16, rt, sizeof(int) * 64) * num_cus();
     }
-    const int64_t max_len = kv->max_seq_len;
     const int64_t max_splits = cdiv(max_len, step);
     int64_t splits;
     if (opt && opt->num_splits > 0) {
         splits = opt->num_splits;
     } else {
         const int64_t units = (int64_t)kv->num_seqs * kv->n_kv_heads * n_rtiles;
-        const int64_t target = 8LL * num_cus();
-        const int64_t MIN_STEPS = 2;
         splits = cdiv(target, units);
-        splits = std::min<int64_t>(splits, cdiv(max_len, MIN_STEPS * step));
-        if (splits < 1) splits = 1;
     }
     splits = std::min<int64_t>(splits, max_splits);
     splits = std::max<int64_t>(splits, cdiv(max_len, max_keys));   // per-split staging limit
@@ -180,12 +189,20 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     return KVD_OK;
 }
 
+// Partial-output region sizes (floats) of a plan: o and (m, l).
+void partial_sizes(const kvd_paged_kv* kv, const Plan& p, size_t* n_o, size_t* n_ml) {
+    size_t rows = 0;
+    if (p.splits > 1) rows = (size_t)kv->num_seqs * kv->q_tokens_per_seq * kv->n_q_heads * p.splits;
+    *n_o = rows * kv->head_dim;
+    *n_ml = rows * 2;
+}
+
 size_t workspace_for(const kvd_paged_kv* kv, const Plan& p) {
-    if (p.splits <= 1) return 0;
-    const size_t rows = (size_t)kv->num_seqs * kv->q_tokens_per_seq * kv->n_q_heads;
-    size_t o = rows * p.splits * kv->head_dim * sizeof(float);
-    o = (o + 255) & ~size_t(255);
-    return o + rows * p.splits * 2 * sizeof(float);
+    size_t n_o, n_ml;
+    partial_sizes(kv, p, &n_o, &n_ml);
+    if (n_o == 0) return 0;
+    const size_t o = (n_o * sizeof(float) + 255) & ~size_t(255);
+    return o + n_ml * sizeof(float);
 }
 
 }  // namespace
@@ -299,10 +316,10 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv* kv, const float* q_rot, floa
     a.out = out;
     a.part_o = nullptr;
     a.part_ml = nullptr;
-    if (p.splits > 1) {
-        const size_t rows = (size_t)kv->num_seqs * kv->q_tokens_per_seq * kv->n_q_heads;
-        size_t o = rows * p.splits * kv->head_dim * sizeof(float);
-        o = (o + 255) & ~size_t(255);
+    if (need > 0) {
+        size_t n_o, n_ml;
+        partial_sizes(kv, p, &n_o, &n_ml);
+        const size_t o = (n_o * sizeof(float) + 255) & ~size_t(255);
         a.part_o = (float*)workspace;
         a.part_ml = (float*)((char*)workspace + o);
     }

@@ -59,5 +59,10 @@ constexpr int VALU_MAX_STAGED_BLOCKS = 4096;
 int valu_max_split_keys(int log2_bs);
 bool mfma_supported(int D, int kv_bf16, int rows);
 int mfma_step_keys();
+// Resident workgroups per CU for a kernel variant (occupancy query on the
+// current device; a conservative default when there is none).
+int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds);
+// Query rows (g*T) from which the matrix-core kernel is the default.
+constexpr int MFMA_MIN_ROWS = 2;
 
 }  // namespace kvd

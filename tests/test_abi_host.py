@@ -138,16 +138,31 @@ def test_plan_covers_every_key(max_len, B, T, Hq, Hkv):
     d = desc(num_seqs=B, q_tokens_per_seq=T, n_q_heads=Hq, n_kv_heads=Hkv,
              max_blocks_per_seq=(max_len + bs - 1) // bs, max_seq_len=max_len)
     for forced in (0, 1, 3, 1000):
-        s, k, _ = _plan(d, forced)
+        s, k, _ = _plan(d, forced, kernel=1)
         assert s >= 1 and k >= 1
         assert s * k >= max_len, "splits must cover every key"
         assert (s - 1) * k < max_len, "no split may start past the longest sequence"
         if forced:
             assert s <= max(forced, -(-max_len // (4094 * bs)))
         ws = kb.lib().kvd_decode_attention_workspace_size_ex(ctypes.byref(d),
-                                                             ctypes.byref(kb.KvdAttnOptions(forced, 0)))
+                                                             ctypes.byref(kb.KvdAttnOptions(forced, 1)))
         rows = B * T * Hq
         if s == 1:
             assert ws == 0
         else:
             assert ws >= rows * s * (128 + 2) * 4
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(16, 1, 32, 8), (4, 1, 64, 8), (32, 4, 32, 8), (64, 1, 16, 8)])
+def test_matrix_core_plan(B, T, Hq, Hkv):
+    """The matrix-core kernel covers every key with its splits and is the
+    automatic choice from 2 query rows per kv head."""
+    d = desc(num_seqs=B, q_tokens_per_seq=T, n_q_heads=Hq, n_kv_heads=Hkv, max_blocks_per_seq=1024,
+             max_seq_len=16384)
+    for forced in (0, 1, 3, 1000):
+        s, k, kern = _plan(d, forced, kernel=2)
+        assert kern == 2 and s * k >= 16384 and (s - 1) * k < 16384
+        if forced:
+            assert s <= forced
+    _, _, kern = _plan(d, 0, 0)
+    assert kern == (2 if (Hq // Hkv) * T >= 2 else 1)
