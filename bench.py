@@ -174,15 +174,125 @@ def copy_calibration(dev, nbytes=CALIB_BYTES):
     torch.cuda.synchronize()
 
 
-def stored_traffic():
+def stored_traffic(workload):
+    """HBM bytes per decode-attention call from the committed counter runs, or
+    None if the kernels changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sources_sha") != kernel_sources_sha():
-        return None   # kernels changed since the counters were taken
-    return t.get("attn_bytes_per_launch")
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_sources_sha") != kernel_sources_sha():
+        return None
+    return entry.get("attn_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- profile summary
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else float("nan")
+
+
+def summarize(prof_dir, workload, commands):
+    """Turn rocprofv3 CSV output (kt/ kernel trace, fetch/ FETCH_SIZE,
+    write/ WRITE_SIZE, util/ utilisation counters) into a markdown summary on
+    stdout and record the calibrated traffic per decode-attention call."""
+    import collections
+    w = workloads.make_workload(workloads.CONFIGS[workload])
+    alg = w.algorithmic_bytes()
+    out = [f"# {workload}: decode-attention kernels on MI355X (rocprofv3)", ""]
+    out += ["Commands (repository root):", "", "```"] + commands + ["```", ""]
+
+    trace = _csv_rows(os.path.join(prof_dir, "kt"), "kernel_trace.csv")
+    dur = collections.defaultdict(list)
+    for r in trace:
+        dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    ours = {k: v for k, v in dur.items() if k.startswith(("attn_", "rope_append"))}
+    out += ["## Kernel durations (--kernel-trace --stats)", "",
+            "| kernel | calls | mean us | median us | min us |", "|---|---|---|---|---|"]
+    for k, v in sorted(ours.items()):
+        out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {_median(v):.2f} | {min(v):.2f} |")
+    attn_names = [k for k in ours if k.startswith("attn_")]
+    attn_us = sum(_median(ours[k]) for k in attn_names)
+    out += ["", f"Decode-attention call (sum of medians of {', '.join(sorted(attn_names))}): "
+                f"{attn_us:.2f} us -> {alg['attention'] / attn_us / 1e3:.0f} GB/s algorithmic "
+                f"({alg['attention'] / attn_us / 1e3 / PEAK_HBM_GBS:.1%} of 8 TB/s).", ""]
+
+    def per_kernel(sub, counter):
+        vals = collections.defaultdict(list)
+        for r in _csv_rows(os.path.join(prof_dir, sub), "counter_collection.csv"):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    calib_kib = CALIB_BYTES / 1024.0
+    f_cal = [x for x in fetch.get("vectorized_elementwise_kernel", []) if x > 0.25 * calib_kib]
+    w_cal = [x for x in write.get("vectorized_elementwise_kernel", []) if x > 0.25 * calib_kib]
+    f_fac = _median(f_cal) / calib_kib if f_cal else float("nan")
+    w_fac = _median(w_cal) / calib_kib if w_cal else float("nan")
+    out += ["## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", "",
+            f"Calibration: a plain fp32 negate of {CALIB_BYTES >> 20} MiB (reads and writes "
+            f"{CALIB_BYTES >> 20} MiB) reads FETCH_SIZE = {_median(f_cal):.0f} KiB "
+            f"(factor {f_fac:.4f}) and WRITE_SIZE = {_median(w_cal):.0f} KiB (factor {w_fac:.4f}); "
+            "counter values below are divided by these factors.", "",
+            "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
+            "|---|---|---|---|---|"]
+    traffic = 0.0
+    for k in sorted(set(fetch) & set(ours)):
+        fk, wk = _median(fetch[k]), _median(write.get(k, [0.0]))
+        rd, wr = fk / f_fac * 1024, wk / w_fac * 1024
+        if k.startswith("attn_"):
+            traffic += rd + wr
+        out.append(f"| {k} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} |")
+    out += ["", f"Decode-attention call: {traffic / 1e6:.2f} MB of HBM traffic vs "
+                f"{alg['attention'] / 1e6:.2f} MB algorithmic ({traffic / alg['attention']:.3f}x).", ""]
+
+    util = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv_rows(os.path.join(prof_dir, "util"), "counter_collection.csv"):
+        util[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if util:
+        out += ["## Utilisation (one --pmc run)", "",
+                "GRBM_GUI_ACTIVE is summed over the 8 XCDs by the collector; per-XCD cycles = sum / 8. "
+                "VALU busy = SQ_ACTIVE_INST_VALU / (256 CUs x cycles); MFMA busy = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles).", "",
+                "| kernel | cycles | VALU busy | MFMA busy | VALU instr / wave | LDS bank conflicts |",
+                "|---|---|---|---|---|---|"]
+        for k in sorted(util):
+            if not k.startswith("attn_"):
+                continue
+            m = {c: _median(v) for c, v in util[k].items()}
+            cyc = m.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+            out.append(f"| {k} | {cyc:.0f} | {m.get('SQ_ACTIVE_INST_VALU', 0) / 256 / cyc:.1%} | "
+                       f"{m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / 1024 / cyc:.2%} | "
+                       f"{m.get('SQ_INSTS_VALU', 0) / max(m.get('SQ_WAVES', 1), 1):.0f} | "
+                       f"{m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+        out.append("")
+    print("\n".join(out))
+
+    entry = {"kernel_sources_sha": kernel_sources_sha(), "attn_bytes_per_launch": round(traffic),
+             "fetch_factor": f_fac, "write_factor": w_fac, "attn_us_trace": attn_us}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {}
+    allt[workload] = entry
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allt, f, indent=1, sort_keys=True)
 
 
 def main():
@@ -196,7 +306,14 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize", metavar="PROFILE_DIR",
+                    help="write the profile summary of rocprofv3 output in PROFILE_DIR and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="(with --summarize) a profiling command to quote in the summary")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.workload, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence, kv head or key range with no exchange inside the "
@@ -222,7 +339,7 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     s = w.spec
-    traffic = stored_traffic()
+    traffic = stored_traffic(args.workload)
     line = {
         "metric": "decode-attention tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
         "value": head["tokens_per_s"],
