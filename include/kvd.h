@@ -157,7 +157,8 @@ int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options
  *   softmax_scale  scale; 0 means 1/sqrt(D).
  *   workspace      device scratch of at least kvd_decode_attention_workspace_size
  *                  bytes (may be NULL when that is 0), 256-byte aligned.  Its
- *                  contents need no initialisation and are clobbered.
+ *                  contents need no initialisation and are clobbered; calls
+ *                  that share a workspace must not run concurrently.
  *
  * Accumulation is fp32; the cache is read in kv_dtype.  Cache slots past
  * seq_lens (tail slots, unused blocks) are never read, whatever they hold.

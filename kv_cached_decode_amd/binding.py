@@ -232,15 +232,16 @@ _ws_cache = {}
 
 
 def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO):
-    """A cached device workspace big enough for this descriptor (None if none
-    is needed).  Allocation happens here, outside the library."""
+    """A cached, zero-initialised device workspace big enough for this
+    descriptor (None if none is needed).  Allocation happens here, outside
+    the library; the library leaves its counters at zero after every call."""
     n = decode_attention_workspace_size(kv, num_splits, kernel)
     if n == 0:
         return None
     dev = kv.k_cache.device
     buf = _ws_cache.get(dev)
     if buf is None or buf.numel() < n:
-        buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        buf = torch.zeros(n, dtype=torch.uint8, device=dev)
         _ws_cache[dev] = buf
     return buf
 

@@ -197,13 +197,23 @@ void partial_sizes(const kvd_paged_kv* kv, const Plan& p, size_t* n_o, size_t* n
     *n_ml = rows * 2;
 }
 
-size_t workspace_for(const kvd_paged_kv* kv, const Plan& p) {
+// Workspace carve-up: [partial o | partial (m, l)], 256-byte aligned.
+struct Carve {
+    size_t o, ml, total;
+};
+
+Carve carve(const kvd_paged_kv* kv, const Plan& p) {
+    Carve c{0, 0, 0};
     size_t n_o, n_ml;
     partial_sizes(kv, p, &n_o, &n_ml);
-    if (n_o == 0) return 0;
-    const size_t o = (n_o * sizeof(float) + 255) & ~size_t(255);
-    return o + n_ml * sizeof(float);
+    if (n_o == 0) return c;
+    c.o = 0;
+    c.ml = (n_o * sizeof(float) + 255) & ~size_t(255);
+    c.total = c.ml + n_ml * sizeof(float);
+    return c;
 }
+
+size_t workspace_for(const kvd_paged_kv* kv, const Plan& p) { return carve(kv, p).total; }
 
 }  // namespace
 
@@ -317,11 +327,9 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv* kv, const float* q_rot, floa
     a.part_o = nullptr;
     a.part_ml = nullptr;
     if (need > 0) {
-        size_t n_o, n_ml;
-        partial_sizes(kv, p, &n_o, &n_ml);
-        const size_t o = (n_o * sizeof(float) + 255) & ~size_t(255);
-        a.part_o = (float*)workspace;
-        a.part_ml = (float*)((char*)workspace + o);
+        const Carve cv = carve(kv, p);
+        a.part_o = (float*)((char*)workspace + cv.o);
+        a.part_ml = (float*)((char*)workspace + cv.ml);
     }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s) : kvd::launch_attn_valu(a, s);

@@ -196,3 +196,30 @@ def test_each_kernel_family(name, kernel):
     _, ref, _, _ = oracle_step(w)
     e = assert_parity(spec, out, ref)
     print(f"{name} kernel {kernel}: error {e:.3e}")
+
+
+@needs_gpu
+def test_one_workspace_across_shapes():
+    """One workspace, never cleared, serves calls of any shape and kernel;
+    repeated calls give identical results (it holds only scratch partials)."""
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")
+    cases = []
+    for name, kernel, splits in [("llama3_8b", 2, 3), ("qwen3_0_6b_cb", 2, 4), ("llama3_8b", 1, 5),
+                                 ("mtp_verify", 2, 6), ("llama3_8b", 2, 3)]:
+        spec = workloads.small_variant(name)
+        w = cached_workload(spec)
+        case = GpuCase(w)
+        q_rot = kb.rope_append_kv(case.kv, case.q, case.k, case.v, rope_base=spec.rope_base)
+        need = kb.decode_attention_workspace_size(case.kv, splits, kernel)
+        assert 0 < need <= ws.numel()
+        note("workspace reuse", name, kernel, splits)
+        outs = []
+        for _ in range(3):
+            out = kb.decode_attention(case.kv, q_rot, workspace_buf=ws, num_splits=splits, kernel=kernel)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert all(np.array_equal(outs[0], o) for o in outs[1:])
+        cases.append((spec, w, outs[0]))
+    for spec, w, out in cases:
+        _, ref, _, _ = oracle_step(w)
+        assert_parity(spec, out, ref)
