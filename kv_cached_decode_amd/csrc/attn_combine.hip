@@ -15,10 +15,11 @@
 namespace kvd {
 namespace {
 
-// One workgroup of COMBINE_THREADS per query row.  The split weights
+// One workgroup of COMBINE_THREADS per query row.  Up to 8 splits, each
+// thread reads everything it needs in one go; beyond that the split weights
 // 2^(m_s - M) / sum are formed once in LDS (lanes over splits, wave
-// reductions), then each thread owns head-dimension elements and sums its
-// splits with independent loads in flight.
+// reductions), then each thread sums its splits with independent loads in
+// flight.
 constexpr int COMBINE_THREADS = 128;
 constexpr int MAX_STAGED_SPLITS = 1024;
 
@@ -34,6 +35,42 @@ __device__ inline float wave_sum(float x) {
     return x;
 }
 
+// Few splits (the common case): every thread loads its own elements and all
+// (m, l) pairs at once, so the kernel costs one memory round trip.
+template <int NMAX>
+__device__ inline bool combine_small(const AttnArgs& a, size_t qrow, int n) {
+    if (n > NMAX) return false;
+    const CacheView& c = a.c;
+    const int S = a.num_splits;
+    const float* ml = a.part_ml + qrow * S * 2;
+    const float* po = a.part_o + qrow * S * c.D;
+    for (int d = threadIdx.x; d < c.D; d += COMBINE_THREADS) {
+        float m[NMAX], l[NMAX], o[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s) {
+            if (s < n) {
+                m[s] = ml[2 * s];
+                l[s] = ml[2 * s + 1];
+                o[s] = po[(size_t)s * c.D + d];
+            }
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if (s < n) M = fmaxf(M, m[s]);
+        float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if (s < n) {
+                const float w = exp2f(m[s] - M);
+                Ls += l[s] * w;
+                O += o[s] * w;
+            }
+        a.out[qrow * c.D + d] = O / Ls;
+    }
+    return true;
+}
+
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs a) {
     __shared__ float sm_w[MAX_STAGED_SPLITS];
     __shared__ float sm_red[2];
@@ -43,6 +80,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     const int L = c.seq_lens[b];
     const int S = a.num_splits;
     const int n = min(S, (L + a.split_keys - 1) / a.split_keys);
+    if (combine_small<8>(a, qrow, n)) return;
     const float* ml = a.part_ml + qrow * S * 2;
     const float* po = a.part_o + qrow * S * c.D;
 

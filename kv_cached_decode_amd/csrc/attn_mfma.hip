@@ -75,17 +75,13 @@ __device__ inline float xor_sum(float x) {
 // slot z of the grid takes the z-th longest sequence (ties by index).  With a
 // ragged batch the longest units start first and the short ones fill the
 // gaps (longest-processing-time-first list scheduling); a uniform batch keeps
-// its natural order.  Computed per workgroup from seq_lens (each thread ranks
-// one sequence against all others), for batches up to LPT_MAX_SEQS; larger
-// batches keep their natural order.
-__device__ inline int lpt_sequence(const CacheView& c, int z, int* sm_len, int* sm_pick) {
-    if (c.B > LPT_MAX_SEQS) return z;
-    for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];
-    __syncthreads();
-    for (int b = threadIdx.x; b < c.B; b += blockDim.x) {
+// its natural order.  Each thread ranks one sequence against all the others
+// (batches up to LPT_MAX_SEQS; larger ones keep their natural order).
+__device__ inline int lpt_rank_pick(int B, int z, const int* sm_len, int* sm_pick) {
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
         const int Lb = sm_len[b];
         int rank = 0;
-        for (int i = 0; i < c.B; ++i) {
+        for (int i = 0; i < B; ++i) {
             const int Li = sm_len[i];
             rank += (Li > Lb) | ((Li == Lb) & (i < b));
         }
@@ -113,38 +109,65 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int j = lane >> 4;            // lane group
     const int split = blockIdx.x;
     const int kvh = blockIdx.y;
-    // the LPT ranking borrows the V-tile LDS (unused until the key loop)
-    const int b = lpt_sequence(c, blockIdx.z, (int*)sm_v, &sm_pick);
-
-    const int L = c.seq_lens[b];
+    const int z = blockIdx.z;
     const int key_begin = split * a.split_keys;
-    if (key_begin >= L) return;         // empty split: the combine skips it
-    const int key_end = min(L, key_begin + a.split_keys);
-
-    // Q^T operand for row n16 (rows >= M are zero): dims 32*kk + 8*j .. +8,
-    // scaled into log2 units and split into bf16 hi + lo.
-    const int row = n16;
+    const int row = n16;                // query row of this lane (rows >= M are padding)
     const bool row_ok = row < a.rows;
     const int t_row = row_ok ? row / c.g : 0;
     const int h_row = kvh * c.g + (row_ok ? row - t_row * c.g : 0);
-    const int vis = row_ok ? L - c.T + t_row : L - 1;     // last key this row sees
-    bf16x8 qhi[4], qlo[4];
-    {
-        const float* qp = a.q + (((size_t)b * c.T + t_row) * c.Hq + h_row) * D;
+
+    // Loads that depend on the sequence: its length, this lane's q slice and
+    // the block ids of the split's first piece (one per thread).  They are
+    // issued for slot z before the longest-first ranking is known -- the
+    // ranking keeps uniform batches in place -- and redone if it moves z.
+    float xq[4][8];
+    int tb = 0;
+    auto load_seq = [&](int bb, int LL) {
+        const float* qp = a.q + (((size_t)bb * c.T + t_row) * c.Hq + h_row) * D;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const float4 x0 = *(const float4*)(qp + 32 * kk + 8 * j);
             const float4 x1 = *(const float4*)(qp + 32 * kk + 8 * j + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = row_ok ? xs[e] * a.scale_log2 : 0.0f;
-                const __bf16 hi = (__bf16)v;
-                qhi[kk][e] = hi;
-                qlo[kk][e] = (__bf16)(v - (float)hi);
-            }
+            xq[kk][0] = x0.x; xq[kk][1] = x0.y; xq[kk][2] = x0.z; xq[kk][3] = x0.w;
+            xq[kk][4] = x1.x; xq[kk][5] = x1.y; xq[kk][6] = x1.z; xq[kk][7] = x1.w;
+        }
+        if (key_begin < LL) {
+            const int blk0 = key_begin >> c.log2_bs;
+            const int last = min(LL, key_begin + a.split_keys) - 1;
+            const int nblk = min((last >> c.log2_bs) - blk0 + 1, MAX_PIECE_BLOCKS);
+            if ((int)threadIdx.x < nblk) tb = c.table[(size_t)bb * c.max_blocks + blk0 + threadIdx.x];
+        }
+    };
+    int b = z;
+    int L = c.seq_lens[z];
+    load_seq(z, L);
+    if (c.B > 1 && c.B <= LPT_MAX_SEQS) {
+        // the ranking borrows the V-tile LDS (unused until the key loop)
+        int* sm_len = (int*)sm_v;
+        for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];
+        __syncthreads();
+        b = lpt_rank_pick(c.B, z, sm_len, &sm_pick);
+        if (b != z) {
+            L = sm_len[b];
+            load_seq(b, L);
         }
     }
+    if (key_begin >= L) return;         // empty split: the combine skips it
+    const int key_end = min(L, key_begin + a.split_keys);
+    const int vis = row_ok ? L - c.T + t_row : L - 1;     // last key this row sees
+
+    // Q^T operand for row n16: dims 32*kk + 8*j .. +8, scaled into log2 units
+    // and split into bf16 hi + lo.
+    bf16x8 qhi[4], qlo[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = row_ok ? xq[kk][e] * a.scale_log2 : 0.0f;
+            const __bf16 hi = (__bf16)v;
+            qhi[kk][e] = hi;
+            qlo[kk][e] = (__bf16)(v - (float)hi);
+        }
 
     const char* kbase = (const char*)c.k;
     const char* vbase = (const char*)c.v;
@@ -163,7 +186,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         const int nblk = ((p1 - 1) >> c.log2_bs) - blk0 + 1;
         const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
         __syncthreads();                      // the previous piece (or the ranking) is done with LDS
-        for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+        if (p0 == key_begin) {
+            // first piece: thread i already holds block id i
+            if ((int)threadIdx.x < nblk) sm_blk[threadIdx.x] = tb;
+            for (int i = threadIdx.x + blockDim.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+        } else {
+            for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+        }
         __syncthreads();
 
         auto row_addr = [&](const char* base, int key) -> const char* {

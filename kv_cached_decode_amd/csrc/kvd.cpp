@@ -181,7 +181,9 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     splits = std::min<int64_t>(splits, max_splits);
     splits = std::max<int64_t>(splits, cdiv(max_len, max_keys));   // per-split staging limit
     if (splits < 1) splits = 1;
-    int64_t keys = cdiv(cdiv(max_len, splits), step) * step;
+    // equal shares (the kernels clamp a range that is not a multiple of their
+    // step, so no rounding that would load the first splits more)
+    int64_t keys = cdiv(max_len, splits);
     splits = cdiv(max_len, keys);
     if (splits > 65535) return fail(KVD_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)splits);
     p->splits = (int)splits;

@@ -38,42 +38,60 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const int token = blockIdx.x;
     const int b = token / c.T, t = token - b * c.T;
     const int D = c.D, half = D >> 1;
-    const int pos = c.seq_lens[b] - c.T + t;
-
-    for (int i = threadIdx.x; i < half; i += blockDim.x) {
-        double theta = pow(a.base, -2.0 * (double)i / (double)D);
-        double phi = (double)pos * theta;
-        cs[i] = cos(phi);
-        sn[i] = sin(phi);
-    }
-    __syncthreads();
-
     const int heads_per_wg = blockDim.x / half;
     const int head = blockIdx.y * heads_per_wg + (int)threadIdx.x / half;
     const int i = (int)threadIdx.x % half;
-    if ((int)threadIdx.x >= heads_per_wg * half || head >= c.Hq + 2 * c.Hkv) return;
-
+    const bool active = (int)threadIdx.x < heads_per_wg * half && head < c.Hq + 2 * c.Hkv;
     int ia, ic;
     pair_of(i, half, a.interleaved, ia, ic);
+
+    // This thread's inputs first (they do not depend on the angles), so their
+    // latency overlaps the fp64 angle evaluation below.
+    float x0 = 0.0f, x1 = 0.0f;
+    if (active) {
+        if (head < c.Hq) {
+            const size_t o = ((size_t)token * c.Hq + head) * D;
+            x0 = a.q[o + ia];
+            x1 = a.q[o + ic];
+        } else if (head < c.Hq + c.Hkv) {
+            const size_t o = ((size_t)token * c.Hkv + (head - c.Hq)) * D;
+            x0 = a.k[o + ia];
+            x1 = a.k[o + ic];
+        } else {
+            const size_t o = ((size_t)token * c.Hkv + (head - c.Hq - c.Hkv)) * D + 2 * i;
+            x0 = a.v[o];
+            x1 = a.v[o + 1];
+        }
+    }
+    const int pos = c.seq_lens[b] - c.T + t;
+    const int blk = c.table[(size_t)b * c.max_blocks + (pos >> c.log2_bs)];
+
+    for (int p = threadIdx.x; p < half; p += blockDim.x) {
+        double theta = pow(a.base, -2.0 * (double)p / (double)D);
+        double phi = (double)pos * theta;
+        cs[p] = cos(phi);
+        sn[p] = sin(phi);
+    }
+    __syncthreads();
+    if (!active) return;
+
     if (head < c.Hq) {
         // query -> q_rot (fp32); q and q_rot may alias: the pair is read and
         // written by this thread only.
         const size_t o = ((size_t)token * c.Hq + head) * D;
         double xr, yr;
-        rotate(a.q[o + ia], a.q[o + ic], cs[i], sn[i], xr, yr);
+        rotate(x0, x1, cs[i], sn[i], xr, yr);
         a.q_rot[o + ia] = (float)xr;
         a.q_rot[o + ic] = (float)yr;
         return;
     }
     // the cache slot of this token
-    const int blk = c.table[(size_t)b * c.max_blocks + (pos >> c.log2_bs)];
     const int off = pos & ((1 << c.log2_bs) - 1);
     if (head < c.Hq + c.Hkv) {
         const int h = head - c.Hq;
-        const size_t src = ((size_t)token * c.Hkv + h) * D;
         const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
         double xr, yr;
-        rotate(a.k[src + ia], a.k[src + ic], cs[i], sn[i], xr, yr);
+        rotate(x0, x1, cs[i], sn[i], xr, yr);
         if (a.kv_bf16) {
             uint16_t* kc = (uint16_t*)c.k;
             kc[dst + ia] = bf16_from_f64(xr);
@@ -85,19 +103,15 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
         }
     } else {
         const int h = head - c.Hq - c.Hkv;
-        const size_t src = ((size_t)token * c.Hkv + h) * D;
-        const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
-        // two consecutive elements per thread
-        const int d = 2 * i;
-        const float v0 = a.v[src + d], v1 = a.v[src + d + 1];
+        const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D + 2 * i;
         if (a.kv_bf16) {
             uint16_t* vc = (uint16_t*)c.v;
-            vc[dst + d] = bf16_from_f32(v0);
-            vc[dst + d + 1] = bf16_from_f32(v1);
+            vc[dst] = bf16_from_f32(x0);
+            vc[dst + 1] = bf16_from_f32(x1);
         } else {
             float* vc = (float*)c.v;
-            vc[dst + d] = v0;
-            vc[dst + d + 1] = v1;
+            vc[dst] = x0;
+            vc[dst + 1] = x1;
         }
     }
 }
