@@ -223,3 +223,49 @@ def test_one_workspace_across_shapes():
     for spec, w, out in cases:
         _, ref, _, _ = oracle_step(w)
         assert_parity(spec, out, ref)
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["llama3_8b", "mtp_verify", "valu_f32"])
+def test_step_replays_under_hip_graph_capture(name):
+    """The whole step (RoPE+append, attention, split merge) captured in a HIP
+    graph: every replay, with eager work and synchronisations in between,
+    matches the eager result bit for bit."""
+    if name == "valu_f32":
+        spec = workloads.Spec("graph_valu_f32", 3, 2, 8, 2, 64, 16, "f32", (600, 5000), 10000.0,
+                              "normal", "shuffled", spare_frac=0.1, seed=77)
+        w = workloads.make_workload(spec)
+        assert kb.decode_attention_plan(GpuCase(w).kv)[0] > 1, "want a split plan"
+    else:
+        spec = workloads.small_variant(name)
+        w = cached_workload(spec)
+    note("graph", name)
+    case = GpuCase(w)
+    q_rot = torch.empty_like(case.q)
+    out = torch.empty_like(case.q)
+    ws = kb.workspace(case.kv)
+    ws = ws.clone() if ws is not None else None
+
+    def step():
+        kb.rope_append_kv(case.kv, case.q, case.k, case.v, q_rot, rope_base=spec.rope_base,
+                          layout=spec.layout)
+        kb.decode_attention(case.kv, q_rot, out, workspace_buf=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {i} differs from eager"
+        step()                       # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager)
