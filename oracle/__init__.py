@@ -32,6 +32,7 @@ class _Cache(ctypes.Structure):
         ("v_pool", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -90,7 +91,7 @@ class OracleCache:
     """
 
     def __init__(self, *, num_seqs, q_tokens, n_q_heads, n_kv_heads, head_dim, block_size,
-                 k_pool, v_pool, block_table, seq_lens, cache_dtype):
+                 k_pool, v_pool, block_table, seq_lens, cache_dtype, window=0):
         self.cache_dtype = cache_dtype
         dt = _DTYPES[cache_dtype]
         self.k_pool = _req(k_pool, dt)
@@ -104,7 +105,7 @@ class OracleCache:
                          self.head_dim, self.block_size, int(self.k_pool.shape[0]),
                          int(self.block_table.shape[1]) if self.block_table.ndim == 2 else 0,
                          cache_dtype, _ptr(self.k_pool), _ptr(self.v_pool),
-                         _ptr(self.block_table), _ptr(self.seq_lens))
+                         _ptr(self.block_table), _ptr(self.seq_lens), int(window))
 
     def rope_append_kv(self, q, k, v, base, layout=ROPE_HALF):
         q = _req(q, np.float32)

@@ -16,8 +16,10 @@
  *       slot = pool[table[b][pos / bs]][kvh][pos % bs][:].
  *
  *   Attention (generate.rs `mha_decode_t(q, k, v, hq, hkv, dh, s)`, GQA as in
- *   the ferrox `decoder` module):
- *       s_j = scale * <q_rot, K_j>, j = 0 .. seq_lens[b] - T + t,
+ *   the ferrox `decoder` module; the sliding window of the ferrox
+ *   `kv_budget::SlidingWindow` type limits it to the last `window` keys):
+ *       s_j = scale * <q_rot, K_j>, j = j0 .. p, p = seq_lens[b] - T + t,
+ *       j0 = 0, or max(0, p - window + 1) with a window,
  *       out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s),
  *       kv head of query head h = h / (Hq / Hkv).
  */
@@ -123,7 +125,7 @@ static int check_cache(const oracle_cache *c)
     if (!c || c->num_seqs < 0 || c->q_tokens < 1 || c->n_q_heads < 1 ||
         c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads != 0 ||
         c->head_dim < 2 || c->head_dim % 2 != 0 || c->block_size < 1 ||
-        c->num_blocks < 0 || c->max_blocks_per_seq < 0)
+        c->num_blocks < 0 || c->max_blocks_per_seq < 0 || c->window < 0)
         return 1;
     if (c->cache_dtype != ORACLE_F32 && c->cache_dtype != ORACLE_BF16 &&
         c->cache_dtype != ORACLE_F64)
@@ -217,18 +219,20 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
     return 0;
 }
 
-/* One query row: q (D values) of sequence b against keys 0 .. n_vis-1 of kv
- * head kvh.  Writes out[D], *lse and *wsum. */
+/* One query row: q (D values) of sequence b against keys j0 .. n_vis-1 of kv
+ * head kvh, j0 = 0 or the start of the sliding window.  Writes out[D], *lse
+ * and *wsum. */
 static int attend_row(const oracle_cache *c, int32_t b, int32_t kvh,
                       int64_t n_vis, const double *q, double scale,
                       double *out, double *lse, double *wsum)
 {
     const int32_t D = c->head_dim;
+    const int64_t j0 = (c->window > 0 && n_vis > c->window) ? n_vis - c->window : 0;
     double *s = (double *)malloc(sizeof(double) * (size_t)n_vis);
     if (!s)
         return 2;
     double m = -INFINITY;
-    for (int64_t j = 0; j < n_vis; ++j) {
+    for (int64_t j = j0; j < n_vis; ++j) {
         size_t idx = slot_index(c, b, j, kvh);
         double dot = 0.0;
         for (int32_t d = 0; d < D; ++d)
@@ -238,14 +242,14 @@ static int attend_row(const oracle_cache *c, int32_t b, int32_t kvh,
             m = s[j];
     }
     double denom = 0.0;
-    for (int64_t j = 0; j < n_vis; ++j) {
+    for (int64_t j = j0; j < n_vis; ++j) {
         s[j] = exp(s[j] - m);   /* unnormalised weight */
         denom += s[j];
     }
     for (int32_t d = 0; d < D; ++d)
         out[d] = 0.0;
     double total = 0.0;
-    for (int64_t j = 0; j < n_vis; ++j) {
+    for (int64_t j = j0; j < n_vis; ++j) {
         size_t idx = slot_index(c, b, j, kvh);
         double w = s[j] / denom;
         total += w;

@@ -58,6 +58,9 @@ typedef struct {
     void *v_pool;               /* [num_blocks][Hkv][bs][D] */
     const int32_t *block_table; /* [B][max_blocks_per_seq] */
     const int32_t *seq_lens;    /* [B] keys per sequence, new tokens included */
+    int32_t window;             /* sliding window in keys (0 = whole cache): the
+                                   query at position p sees keys
+                                   max(0, p - window + 1) .. p */
 } oracle_cache;
 
 /* Return codes: 0 ok, nonzero = bad descriptor (nothing written). */
@@ -77,7 +80,8 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
                           double base, int32_t layout);
 
 /* Attention of every query row against the cache as it stands.  Query t of
- * sequence b sees keys 0 .. seq_lens[b] - T + t (inclusive).  out:
+ * sequence b sees keys 0 .. seq_lens[b] - T + t (inclusive), or the last
+ * `window` of them.  out:
  * [B][T][Hq][D]; lse (optional, may be NULL): [B][T][Hq] natural-log
  * log-sum-exp of the scaled scores; wsum (optional): [B][T][Hq] sum of the
  * normalised softmax weights (1 up to rounding). */

@@ -430,6 +430,44 @@ def check_verify_row_equals_shorter_decode():
         assert np.array_equal(out[:, t], o1[:, 0]), t
 
 
+def check_sliding_window_equals_truncated_cache():
+    """Attention with a window of W keys equals full attention over a cache
+    that holds only the last W keys of each sequence (the same stored rows,
+    moved to positions 0..W-1), and a verify row with a window equals the
+    shorter single-token decode with the same window."""
+    for W in (1, 5, 33, 200):
+        w, oc = _tiny_cache(B=3, T=1, L=(0, 120), seed=14)
+        s = w.spec
+        q = w.q.astype(np.float64)
+        out_w = oracle_cache(w, k_pool=oc.k_pool, v_pool=oc.v_pool, dtype="f64", window=W).decode_attention(q)
+        bs = s.block_size
+        keep = [min(int(L), W) for L in w.seq_lens]
+        nblk = max((k + bs - 1) // bs for k in keep)
+        kp = np.full((s.num_seqs * nblk, s.n_kv_heads, bs, s.head_dim), np.nan)
+        vp = np.full_like(kp, np.nan)
+        table = np.arange(s.num_seqs * nblk, dtype=np.int32).reshape(s.num_seqs, nblk)
+        for b in range(s.num_seqs):
+            L = int(w.seq_lens[b])
+            for new, old in enumerate(range(L - keep[b], L)):
+                blk = w.block_table[b, old // bs]
+                kp[table[b, new // bs], :, new % bs] = oc.k_pool[blk, :, old % bs]
+                vp[table[b, new // bs], :, new % bs] = oc.v_pool[blk, :, old % bs]
+        trunc = oracle.OracleCache(num_seqs=s.num_seqs, q_tokens=1, n_q_heads=s.n_q_heads,
+                                   n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, block_size=bs,
+                                   k_pool=kp, v_pool=vp, block_table=table,
+                                   seq_lens=np.array(keep, np.int32), cache_dtype=oracle.ORACLE_F64)
+        assert np.array_equal(out_w, trunc.decode_attention(q)), W
+    T = 3
+    w, oc = _tiny_cache(B=2, T=T, L=(4, 60), seed=15)
+    q = w.q.astype(np.float64)
+    out = oracle_cache(w, k_pool=oc.k_pool, v_pool=oc.v_pool, dtype="f64", window=7).decode_attention(q)
+    for t in range(T):
+        sl = (w.seq_lens - (T - 1 - t)).astype(np.int32)
+        one = oracle_cache(w, seq_lens=sl, q_tokens=1, k_pool=oc.k_pool, v_pool=oc.v_pool, dtype="f64",
+                           window=7)
+        assert np.array_equal(out[:, t], one.decode_attention(np.ascontiguousarray(q[:, t:t + 1]))[:, 0])
+
+
 def check_rows_api():
     w, oc = _tiny_cache(B=3, T=2, L=(3, 40), seed=13)
     q = w.q.astype(np.float64)

@@ -30,6 +30,7 @@ MUTANTS = {
     "ties_away": ("double n = nearbyint(a / quantum);", "double n = floor(a / quantum + 0.5);"),
     "double_rounding": ("double a = fabs(x);", "double a = fabs((double)(float)x);"),
     "k_not_rotated": ("store(c, c->k_pool, s + d, y[d]);", "store(c, c->k_pool, s + d, x[d]);"),
+    "window_off_by_one": ("? n_vis - c->window : 0;", "? n_vis - c->window + 1 : 0;"),
 }
 
 
