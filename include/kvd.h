@@ -76,6 +76,11 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *                       can be captured in a HIP graph).
  *                       T <= max_seq_len <= max_blocks_per_seq * bs.
  *   kv_dtype            KVD_KV_BF16 or KVD_KV_F32.
+ *   window              sliding window in keys, 0 = attend the whole cache: the
+ *                       query at position p sees keys max(0, p - window + 1)
+ *                       .. p (the ferrox-models kv_budget SlidingWindow).  The
+ *                       append is unaffected; keys before every query's window
+ *                       are not read.
  *   k_cache, v_cache    [num_blocks][Hkv][bs][D] each, element type kv_dtype,
  *                       16-byte aligned.  Key position p of sequence b lives in
  *                       block block_table[b][p / bs], slot p % bs.
@@ -96,6 +101,7 @@ typedef struct kvd_paged_kv {
     int32_t max_blocks_per_seq;
     int32_t max_seq_len;
     int32_t kv_dtype;
+    int32_t window;
     void *k_cache;
     void *v_cache;
     const int32_t *block_table;
@@ -178,7 +184,7 @@ const char *kvd_status_string(int32_t status);
  * thread-local storage; "" if none). */
 const char *kvd_last_error(void);
 
-/* ABI version, bumped on any incompatible change. */
+/* ABI version, bumped on any incompatible change (2: kvd_paged_kv.window). */
 int32_t kvd_abi_version(void);
 
 #ifdef __cplusplus

@@ -41,6 +41,7 @@ class KvdPagedKV(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
+        ("window", ctypes.c_int32),
         ("k_cache", ctypes.c_void_p),
         ("v_cache", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
@@ -134,6 +135,7 @@ class PagedKV:
     block_table:      int32 [B][max_blocks_per_seq].
     seq_lens:         int32 [B], keys per sequence including the T new tokens.
     max_seq_len:      host-side bound on seq_lens (sizes the split-K plan).
+    window:           sliding window in keys (0 = the whole cache).
     """
     k_cache: torch.Tensor
     v_cache: torch.Tensor
@@ -142,6 +144,7 @@ class PagedKV:
     n_q_heads: int
     q_tokens_per_seq: int
     max_seq_len: int
+    window: int = 0
 
     def __post_init__(self):
         if self.k_cache.dtype not in (torch.bfloat16, torch.float32):
@@ -176,7 +179,7 @@ class PagedKV:
             self.num_seqs, int(self.q_tokens_per_seq), int(self.n_q_heads), self.n_kv_heads,
             self.head_dim, self.block_size, int(self.k_cache.shape[0]),
             int(self.block_table.shape[1]), int(self.max_seq_len),
-            KVD_KV_BF16 if self.k_cache.dtype == torch.bfloat16 else KVD_KV_F32,
+            KVD_KV_BF16 if self.k_cache.dtype == torch.bfloat16 else KVD_KV_F32, int(self.window),
             self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.block_table.data_ptr(),
             self.seq_lens.data_ptr())
 

@@ -6,7 +6,7 @@
 // weighted sum of V.  The row's result is
 //     M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // over the splits that hold keys of this sequence (split s exists when
-// s * split_keys < seq_lens[b]).  Splits whose keys the row cannot see carry
+// range_start + s * split_keys < seq_lens[b]).  Splits whose keys the row cannot see carry
 // l_s = 0 and a very negative m_s, and drop out.
 //
 // Fixed summation order, so results are bitwise reproducible.
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     const int b = (int)(qrow / ((size_t)c.T * c.Hq));
     const int L = c.seq_lens[b];
     const int S = a.num_splits;
-    const int n = min(S, (L + a.split_keys - 1) / a.split_keys);
+    const int n = min(S, (L - range_start(c, L) + a.split_keys - 1) / a.split_keys);
     if (combine_small<8>(a, qrow, n)) return;
     const float* ml = a.part_ml + qrow * S * 2;
     const float* po = a.part_o + qrow * S * c.D;

@@ -25,8 +25,10 @@
 //       O^T keeps the row in l%16, so the per-row rescale is lane-local.
 //
 // Keys past the range are clamped to the range's last key for the loads and
-// masked to weight 0; keys past a draft token's position are masked the
-// same way (causal within the draft).
+// masked to weight 0; keys past a draft token's position, or before its
+// sliding window, are masked the same way (causal within the draft).  Split
+// ranges start at the first key any query can see, so keys before every
+// window are not read.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -110,7 +112,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int split = blockIdx.x;
     const int kvh = blockIdx.y;
     const int z = blockIdx.z;
-    const int key_begin = split * a.split_keys;
     const int row = n16;                // query row of this lane (rows >= M are padding)
     const bool row_ok = row < a.rows;
     const int t_row = row_ok ? row / c.g : 0;
@@ -122,7 +123,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     // ranking keeps uniform batches in place -- and redone if it moves z.
     float xq[4][8];
     int tb = 0;
+    auto split_begin = [&](int LL) { return range_start(c, LL) + split * a.split_keys; };
     auto load_seq = [&](int bb, int LL) {
+        const int key_begin = split_begin(LL);
         const float* qp = a.q + (((size_t)bb * c.T + t_row) * c.Hq + h_row) * D;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -152,9 +155,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
             load_seq(b, L);
         }
     }
+    const int key_begin = split_begin(L);
     if (key_begin >= L) return;         // empty split: the combine skips it
     const int key_end = min(L, key_begin + a.split_keys);
     const int vis = row_ok ? L - c.T + t_row : L - 1;     // last key this row sees
+    const int lo = c.window > 0 ? vis - c.window + 1 : 0;  // first key it sees
 
     // Q^T operand for row n16: dims 32*kk + 8*j .. +8, scaled into log2 units
     // and split into bf16 hi + lo.
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = base + 16 * h + 4 * j + i;
-                    if (key >= p1 || key > vis) s[h][i] = -INFINITY;
+                    if (key >= p1 || key > vis || key < lo) s[h][i] = -INFINITY;
                     mx = fmaxf(mx, s[h][i]);
                 }
             mx = xor_max(mx);

@@ -36,7 +36,8 @@
 //
 // Keys past the sequence end are never loaded (their slots may hold NaN):
 // lanes past the range re-load the range's last key and weight it 0; keys past
-// a draft token's own position get score -inf and weight 0.
+// a draft token's own position, or before its sliding window, get score -inf
+// and weight 0.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     const int b = blockIdx.z;
 
     const int L = c.seq_lens[b];
-    const int key_begin = split * a.split_keys;
+    const int key_begin = range_start(c, L) + split * a.split_keys;
     if (key_begin >= L) return;               // empty split: the combine skips it
     const int key_end = min(L, key_begin + a.split_keys);
 
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 
     // q rows of this tile, pre-scaled into log2 units; row r = t*g + hg.
     float qv[RT][EPL];
-    int vis[RT];
+    int vis[RT], lo[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int row = row0 + r;
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         const int t = ok ? row / c.g : 0;
         const int h = kvh * c.g + (ok ? row - t * c.g : 0);
         vis[r] = ok ? L - c.T + t : -1;       // last visible key (inclusive)
+        lo[r] = c.window > 0 ? vis[r] - c.window + 1 : 0;   // first visible key
         const float4* qp = (const float4*)(a.q + (((size_t)b * c.T + t) * c.Hq + h) * D + chunk * EPL);
 #pragma unroll
         for (int e4 = 0; e4 < EPL / 4; ++e4) {
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc += qv[r][e] * kf[e];
                 acc = group_sum<LPK>(acc);
-                s[u][r] = (j >= key_end || j > vis[r]) ? -INFINITY : acc;
+                s[u][r] = (j >= key_end || j > vis[r] || j < lo[r]) ? -INFINITY : acc;
             }
         }
         // one rescale per step and row

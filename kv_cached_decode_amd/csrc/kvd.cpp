@@ -86,6 +86,7 @@ int32_t check_desc(const kvd_paged_kv* kv) {
                     kv->max_seq_len, (long long)kv->max_blocks_per_seq * kv->block_size);
     if (kv->kv_dtype != KVD_KV_F32 && kv->kv_dtype != KVD_KV_BF16)
         return fail(KVD_ERR_UNSUPPORTED, "kv_dtype = %d", kv->kv_dtype);
+    if (kv->window < 0) return fail(KVD_ERR_SHAPE, "window = %d < 0", kv->window);
     if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens)
         return fail(KVD_ERR_NULL, "k_cache, v_cache, block_table and seq_lens must be non-NULL");
     if (((uintptr_t)kv->k_cache | (uintptr_t)kv->v_cache) & 15)
@@ -109,6 +110,7 @@ kvd::CacheView view_of(const kvd_paged_kv* kv) {
     c.seq_lens = kv->seq_lens;
     c.k = kv->k_cache;
     c.v = kv->v_cache;
+    c.window = kv->window;
     return c;
 }
 
@@ -150,7 +152,11 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     p->kernel = kernel;
 
     const int log2_bs = ilog2(kv->block_size);
-    const int64_t max_len = kv->max_seq_len;
+    // keys a sequence's queries can see at most: the whole cache, or the
+    // window plus the draft
+    const int64_t max_len = kv->window > 0
+        ? std::min<int64_t>(kv->max_seq_len, (int64_t)kv->window + kv->q_tokens_per_seq - 1)
+        : kv->max_seq_len;
     int step, n_rtiles;
     int64_t max_keys = INT32_MAX, target;
     if (kernel == KVD_KERNEL_MFMA) {
@@ -221,7 +227,7 @@ size_t workspace_for(const kvd_paged_kv* kv, const Plan& p) { return carve(kv, p
 
 extern "C" {
 
-int32_t kvd_abi_version(void) { return 1; }
+int32_t kvd_abi_version(void) { return 2; }
 
 const char* kvd_status_string(int32_t s) {
     switch (s) {

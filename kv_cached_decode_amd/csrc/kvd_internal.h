@@ -17,7 +17,15 @@ struct CacheView {
     const int32_t* seq_lens;  // [B]
     void* k;                // [num_blocks][Hkv][bs][D]
     void* v;
+    int32_t window;         // sliding window in keys, 0 = none
 };
+
+// First key any query of a sequence with L keys can see: 0, or the start of
+// the first draft token's window.  Split s of a sequence covers
+// [range_start + s*split_keys, min(L, range_start + (s+1)*split_keys)).
+__device__ inline int range_start(const CacheView& c, int L) {
+    return c.window > 0 ? max(0, L - c.T - c.window + 1) : 0;
+}
 
 struct RopeAppendArgs {
     CacheView c;

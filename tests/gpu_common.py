@@ -38,17 +38,17 @@ def cached_workload(spec):
 class GpuCase:
     """A workload resident on the GPU, ready for the step."""
 
-    def __init__(self, w, seq_lens=None, q_tokens=None):
+    def __init__(self, w, seq_lens=None, q_tokens=None, window=0, block_table=None):
         self.w = w
         s = w.spec
         self.k_cache = to_dev_pool(w.k_pool)
         self.v_cache = to_dev_pool(w.v_pool)
-        self.table = torch.from_numpy(w.block_table).to(DEV)
+        self.table = torch.from_numpy(w.block_table if block_table is None else block_table).to(DEV)
         sl = w.seq_lens if seq_lens is None else seq_lens
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(sl, dtype=np.int32)).to(DEV)
         T = q_tokens or s.q_tokens
         self.kv = kb.PagedKV(self.k_cache, self.v_cache, self.table, self.seq_lens, s.n_q_heads, T,
-                             max(int(np.max(sl)), T) if len(sl) else T)
+                             max(int(np.max(sl)), T) if len(sl) else T, window)
         self.q = torch.from_numpy(w.q).to(DEV)
         self.k = torch.from_numpy(w.k).to(DEV)
         self.v = torch.from_numpy(w.v).to(DEV)
@@ -72,11 +72,11 @@ class GpuCase:
         return to_host_pool(self.k_cache), to_host_pool(self.v_cache)
 
 
-def oracle_step(w, rows=None, scale=None):
+def oracle_step(w, rows=None, scale=None, window=0, block_table=None):
     """Oracle RoPE + append + attention on host copies.  Returns (q_rot fp64,
     out fp64 for all rows or the given flat rows, k_pool, v_pool)."""
     s = w.spec
-    oc = oracle_cache(w)
+    oc = oracle_cache(w, window=window, block_table=block_table)
     q_rot = oc.rope_append_kv(w.q, w.k, w.v, s.rope_base, s.layout)
     if rows is None:
         out = oc.decode_attention(q_rot, scale=scale)

@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     assert kb.status_name(0) == "KVD_OK"
     assert kb.status_name(4) == "KVD_ERR_WORKSPACE"
     assert kb.status_name(99) == "KVD_ERR_UNKNOWN"
-    assert kb.lib().kvd_abi_version() == 1
+    assert kb.lib().kvd_abi_version() == 2
 
 
 FAKE = 0x100000   # never dereferenced: every case below fails validation first
@@ -44,7 +44,7 @@ FAKE = 0x100000   # never dereferenced: every case below fails validation first
 def desc(**kw):
     d = dict(num_seqs=2, q_tokens_per_seq=1, n_q_heads=8, n_kv_heads=2, head_dim=128,
              block_size=16, num_blocks=64, max_blocks_per_seq=8, max_seq_len=100,
-             kv_dtype=kb.KVD_KV_BF16, k_cache=FAKE, v_cache=FAKE + 0x10000, block_table=FAKE + 0x20000,
+             kv_dtype=kb.KVD_KV_BF16, window=0, k_cache=FAKE, v_cache=FAKE + 0x10000, block_table=FAKE + 0x20000,
              seq_lens=FAKE + 0x30000)
     d.update(kw)
     return kb.KvdPagedKV(**d)
@@ -66,6 +66,7 @@ BAD = [
     (dict(q_tokens_per_seq=4, max_seq_len=3), kb.KVD_ERR_SHAPE),
     (dict(max_seq_len=129), kb.KVD_ERR_SHAPE),            # > 8 blocks * 16
     (dict(kv_dtype=2), kb.KVD_ERR_UNSUPPORTED),
+    (dict(window=-1), kb.KVD_ERR_SHAPE),
     (dict(k_cache=0), kb.KVD_ERR_NULL),
     (dict(block_table=0), kb.KVD_ERR_NULL),
     (dict(seq_lens=0), kb.KVD_ERR_NULL),

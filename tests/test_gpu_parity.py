@@ -269,3 +269,73 @@ def test_step_replays_under_hip_graph_capture(name):
         step()                       # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager)
+
+
+WINDOW_CASES = [("llama3_8b", 256), ("qwen3_0_6b_cb", 100), ("mtp_verify", 64), ("long_ctx", 4096),
+                ("llama3_8b", 1), ("qwen3_0_6b_cb", 100000)]
+
+
+@needs_gpu
+@pytest.mark.parametrize("name,window", WINDOW_CASES, ids=[f"{n}-w{w}" for n, w in WINDOW_CASES])
+@pytest.mark.parametrize("kernel", [kb.KVD_KERNEL_VALU, kb.KVD_KERNEL_MFMA], ids=["valu", "mfma"])
+def test_sliding_window(name, window, kernel):
+    """Sliding-window attention (the query at position p sees keys
+    p-W+1 .. p) against the oracle, both kernel families."""
+    spec = workloads.small_variant(name)
+    w = cached_workload(spec)
+    note("window", name, window, kernel)
+    case = GpuCase(w, window=window)
+    _, out = case.step(kernel=kernel)
+    _, ref, _, _ = oracle_step(w, window=window)
+    assert_parity(spec, out, ref)
+
+
+@needs_gpu
+def test_shared_prefix_blocks():
+    """Sequences whose tables point at the same physical blocks for a common
+    prefix (prefix caching): reads are shared, each append lands in the
+    sequence's own last block."""
+    spec = workloads.Spec("shared_prefix", 6, 2, 8, 2, 128, 16, "bf16", (200, 900), 10000.0,
+                          "normal", "shuffled", spare_frac=0.1, seed=31)
+    w = workloads.make_workload(spec)
+    shared = 10                      # 160 keys, below every context
+    table = w.block_table.copy()
+    table[1:, :shared] = table[0, :shared]
+    note("shared prefix")
+    case = GpuCase(w, block_table=table)
+    _, out = case.step()
+    kp, vp = case.pools()
+    _, ref, kp_ref, vp_ref = oracle_step(w, block_table=table)
+    assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref)
+    assert_parity(spec, out, ref)
+
+
+@needs_gpu
+def test_rollback_after_verify():
+    """Verify a 4-token draft, accept 2, roll back by lowering seq_lens, then
+    decode the next token into the rejected slot (the ferrox `engine` cache
+    truncate, done here by the caller's seq_lens alone)."""
+    spec = workloads.Spec("rollback", 4, 4, 16, 4, 128, 16, "bf16", (50, 700), 10000.0, "normal",
+                          "shuffled", spare_frac=0.1, seed=41)
+    w = workloads.make_workload(spec)
+    note("rollback")
+    case = GpuCase(w)
+    case.step()                                   # verify: appends 4 draft tokens
+    oc = oracle_cache(w)
+    oc.rope_append_kv(w.q, w.k, w.v, spec.rope_base)
+    # accept 2 drafts: the next token goes to position ctx + 2
+    sl = (w.ctx_lens + 3).astype(np.int32)
+    rng = np.random.default_rng(7)
+    q1 = rng.standard_normal((spec.num_seqs, 1, spec.n_q_heads, spec.head_dim), dtype=np.float32)
+    k1 = rng.standard_normal((spec.num_seqs, 1, spec.n_kv_heads, spec.head_dim), dtype=np.float32)
+    v1 = rng.standard_normal((spec.num_seqs, 1, spec.n_kv_heads, spec.head_dim), dtype=np.float32)
+    kv1 = kb.PagedKV(case.k_cache, case.v_cache, case.table, torch.from_numpy(sl).cuda(),
+                     spec.n_q_heads, 1, int(sl.max()))
+    q_rot = kb.rope_append_kv(kv1, torch.from_numpy(q1).cuda(), torch.from_numpy(k1).cuda(),
+                              torch.from_numpy(v1).cuda(), rope_base=spec.rope_base)
+    out = kb.decode_attention(kv1, q_rot).cpu().numpy()
+    oc1 = oracle_cache(w, seq_lens=sl, q_tokens=1, k_pool=oc.k_pool, v_pool=oc.v_pool)
+    ref = oc1.decode_attention(oc1.rope_append_kv(q1, k1, v1, spec.rope_base))
+    kp, vp = case.pools()
+    assert np.array_equal(kp, oc1.k_pool) and np.array_equal(vp, oc1.v_pool)
+    assert_parity(spec, out, ref)
