@@ -235,9 +235,9 @@ _ws_cache = {}
 
 
 def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO):
-    """A cached, zero-initialised device workspace big enough for this
-    descriptor (None if none is needed).  Allocation happens here, outside
-    the library; the library leaves its counters at zero after every call."""
+    """A cached device workspace big enough for this descriptor (None if none
+    is needed).  Allocation happens here, outside the library; its contents
+    need no initialisation."""
     n = decode_attention_workspace_size(kv, num_splits, kernel)
     if n == 0:
         return None

@@ -268,3 +268,53 @@ def sample_rows(spec: Spec, n: int, seed: int = 0) -> np.ndarray:
                            np.arange(spec.num_seqs) * per_seq + per_seq - 1])
     extra = rng.choice(total, size=min(n, total), replace=False)
     return np.unique(np.concatenate([ends, extra])).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# The tiny decoder LM of ferric-core `examples/generate.rs` (its `Cfg` and
+# `Layer`): 3 layers, 4 heads of 16, model width 64, MLP width 128, vocab 32,
+# RoPE base 10000, RMSNorm eps 1e-5, prompt [3, 14, 1, 15] then 5 greedy
+# steps.  Weights are seeded uniform draws standing in for the page's hash
+# fill; the norm gains are 1 plus a draw, as on the page.
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class TinyLMConfig:
+    n_layers: int = 3
+    n_heads: int = 4
+    head_dim: int = 16
+    d_model: int = 64
+    d_ff: int = 128
+    vocab: int = 32
+    rope_base: float = 10000.0
+    eps: float = 1e-5
+    weight_scale: float = 0.3
+    seed: int = 9
+
+
+TINY_LM = TinyLMConfig()
+TINY_LM_PROMPT = (3, 14, 1, 15)
+TINY_LM_GEN_STEPS = 5
+
+
+def tiny_lm_weights(cfg: TinyLMConfig = TINY_LM) -> dict:
+    """float32 weights, matrices stored [in][out] (a row vector times W):
+    emb [vocab][d]; per layer wn1, wn2 [d]; wq, wk, wv, wo [d][d]; wg, wu
+    [d][ff]; wd [ff][d]; then wln [d] and wlm [d][vocab]."""
+    rng = np.random.default_rng(cfg.seed)
+    a = cfg.weight_scale
+    d, ff = cfg.d_model, cfg.d_ff
+
+    def u(*shape):
+        return rng.uniform(-a, a, size=shape).astype(np.float32)
+
+    w = {"emb": u(cfg.vocab, d), "layers": []}
+    for _ in range(cfg.n_layers):
+        w["layers"].append({
+            "wn1": (1.0 + u(d)).astype(np.float32), "wn2": (1.0 + u(d)).astype(np.float32),
+            "wq": u(d, d), "wk": u(d, d), "wv": u(d, d), "wo": u(d, d),
+            "wg": u(d, ff), "wu": u(d, ff), "wd": u(ff, d),
+        })
+    w["wln"] = (1.0 + u(d)).astype(np.float32)
+    w["wlm"] = u(d, cfg.vocab)
+    return w
