@@ -2,9 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
 
-A step is one pass of the whole hot path over one batch: kvd_rope_append_kv
-(RoPE at each token's position + paged append) followed by
-kvd_decode_attention (split-K attention + combine), both through the C ABI.
+A step is one pass of the whole hot path over one batch through the C ABI:
+kvd_decode_step, which does RoPE at each token's position, the paged append
+and split-K decode attention (one fused kernel on matrix-core plans, plus the
+split combine).  The same work as two calls (kvd_rope_append_kv, then
+kvd_decode_attention) and the attention call alone are timed beside it.
 The headline workload is the Llama-3-8B-shaped layer (batch 16, 32 q / 8 kv
 heads, head_dim 128, context 4096, bf16 cache).  Inputs are seeded synthetic
 tensors already resident in HBM.  Successive steps rotate over several
@@ -12,8 +14,8 @@ layers' caches (distinct buffers) so that no step finds its cache in the
 256 MB Infinity Cache left behind by the previous one.
 
 Rank 0 prints ONE JSON line.  `value` is tokens/s of the whole step (B*T new
-tokens per step).  `roofline` is for the decode-attention call (the dominant
-kernel): algorithmic bytes per call / its average duration measured with HIP
+tokens per step).  `roofline` is for the step call (the fused kernel and the
+combine): algorithmic bytes per call / its average duration measured with HIP
 events on the launch stream.  `cpu_baseline` times the fp64 oracle on the
 host cores on a bounded sample of the same workload.
 """
@@ -36,7 +38,7 @@ from kv_cached_decode_amd import workloads  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "llama3_8b"
 KERNEL_SOURCES = ["kvd.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_combine.hip", "rope_append.hip",
-                  "kvd_internal.h", "bf16_round.h"]
+                  "kvd_internal.h", "bf16_round.h", "rope_math.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -82,6 +84,12 @@ class Layers:
     def step(self, i):
         kv = self.kv[i % len(self.kv)]
         s = self.w.spec
+        kb.decode_step(kv, self.q, self.k, self.v, self.out, None, False, s.rope_base, s.layout, 0.0,
+                       self.ws, self.num_splits, self.kernel)
+
+    def two_calls(self, i):
+        kv = self.kv[i % len(self.kv)]
+        s = self.w.spec
         kb.rope_append_kv(kv, self.q, self.k, self.v, self.q_rot, s.rope_base, s.layout)
         kb.decode_attention(kv, self.q_rot, self.out, 0.0, self.ws, self.num_splits, self.kernel)
 
@@ -115,13 +123,14 @@ def measure(name, steps, warmup, dev, kernel=0, num_splits=0):
     L = Layers(w, n_layers, dev, kernel, num_splits)
     s = w.spec
     step_ms = timed(L.step, steps, warmup)
+    two_ms = timed(L.two_calls, steps, warmup)
     attn_ms = timed(L.attention, steps, warmup)
     nb = w.algorithmic_bytes()
     tokens = s.num_seqs * s.q_tokens
     res = {
         "workload": name, "layers_rotated": n_layers, "plan": {"splits": L.plan[0], "keys_per_split": L.plan[1],
                                                                "kernel": ["auto", "valu", "mfma"][L.plan[2]]},
-        "step_ms": step_ms, "attn_ms": attn_ms,
+        "step_ms": step_ms, "two_call_step_ms": two_ms, "attn_ms": attn_ms,
         "tokens_per_s": tokens / (step_ms * 1e-3),
         "attn_tokens_per_s": tokens / (attn_ms * 1e-3),
         "attn_bytes": nb["attention"], "step_bytes": nb["step"],
@@ -129,6 +138,7 @@ def measure(name, steps, warmup, dev, kernel=0, num_splits=0):
         "step_GBs": nb["step"] / (step_ms * 1e-3) / 1e9,
     }
     res["attn_frac_of_peak"] = res["attn_GBs"] / PEAK_HBM_GBS
+    res["step_frac_of_peak"] = res["step_GBs"] / PEAK_HBM_GBS
     del L
     torch.cuda.empty_cache()
     return w, res
@@ -175,8 +185,8 @@ def copy_calibration(dev, nbytes=CALIB_BYTES):
 
 
 def stored_traffic(workload):
-    """HBM bytes per decode-attention call from the committed counter runs, or
-    None if the kernels changed since the counters were taken."""
+    """HBM bytes per decode-step call from the committed counter runs, or None
+    if the kernels changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -185,7 +195,7 @@ def stored_traffic(workload):
     entry = t.get(workload)
     if not entry or entry.get("kernel_sources_sha") != kernel_sources_sha():
         return None
-    return entry.get("attn_bytes_per_launch")
+    return entry.get("step_bytes_per_launch")
 
 
 # ---------------------------------------------------------------- profile summary
@@ -212,23 +222,32 @@ def summarize(prof_dir, workload, commands):
     import collections
     w = workloads.make_workload(workloads.CONFIGS[workload])
     alg = w.algorithmic_bytes()
-    out = [f"# {workload}: decode-attention kernels on MI355X (rocprofv3)", ""]
+    out = [f"# {workload}: decode-step kernels on MI355X (rocprofv3)", ""]
     out += ["Commands (repository root):", "", "```"] + commands + ["```", ""]
 
     trace = _csv_rows(os.path.join(prof_dir, "kt"), "kernel_trace.csv")
     dur = collections.defaultdict(list)
     for r in trace:
         dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-    ours = {k: v for k, v in dur.items() if k.startswith(("attn_", "rope_append"))}
+    ours = {k: v for k, v in dur.items() if k.startswith(("attn_", "rope_append", "decode_step"))}
     out += ["## Kernel durations (--kernel-trace --stats)", "",
             "| kernel | calls | mean us | median us | min us |", "|---|---|---|---|---|"]
     for k, v in sorted(ours.items()):
         out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {_median(v):.2f} | {min(v):.2f} |")
+    # the step call: the fused kernel (or RoPE/append + attention) and the
+    # combine; the attention call alone: the attention kernel and the combine
+    combine = [k for k in ours if k.startswith("attn_combine")]
     attn_names = [k for k in ours if k.startswith("attn_")]
+    fused = [k for k in ours if k.startswith("decode_step")]
+    step_names = (fused + combine) if fused else list(ours)
+    step_us = sum(_median(ours[k]) for k in step_names)
     attn_us = sum(_median(ours[k]) for k in attn_names)
-    out += ["", f"Decode-attention call (sum of medians of {', '.join(sorted(attn_names))}): "
-                f"{attn_us:.2f} us -> {alg['attention'] / attn_us / 1e3:.0f} GB/s algorithmic "
-                f"({alg['attention'] / attn_us / 1e3 / PEAK_HBM_GBS:.1%} of 8 TB/s).", ""]
+    out += ["", f"Decode-step call (sum of medians of {', '.join(sorted(step_names))}): "
+                f"{step_us:.2f} us -> {alg['step'] / step_us / 1e3:.0f} GB/s algorithmic "
+                f"({alg['step'] / step_us / 1e3 / PEAK_HBM_GBS:.1%} of 8 TB/s).",
+            f"Decode-attention call alone (sum of medians of {', '.join(sorted(attn_names))}): "
+            f"{attn_us:.2f} us -> {alg['attention'] / attn_us / 1e3:.0f} GB/s algorithmic "
+            f"({alg['attention'] / attn_us / 1e3 / PEAK_HBM_GBS:.1%} of 8 TB/s).", ""]
 
     def per_kernel(sub, counter):
         vals = collections.defaultdict(list)
@@ -250,15 +269,18 @@ def summarize(prof_dir, workload, commands):
             "counter values below are divided by these factors.", "",
             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
             "|---|---|---|---|---|"]
-    traffic = 0.0
+    per_k = {}
     for k in sorted(set(fetch) & set(ours)):
         fk, wk = _median(fetch[k]), _median(write.get(k, [0.0]))
         rd, wr = fk / f_fac * 1024, wk / w_fac * 1024
-        if k.startswith("attn_"):
-            traffic += rd + wr
+        per_k[k] = rd + wr
         out.append(f"| {k} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} |")
-    out += ["", f"Decode-attention call: {traffic / 1e6:.2f} MB of HBM traffic vs "
-                f"{alg['attention'] / 1e6:.2f} MB algorithmic ({traffic / alg['attention']:.3f}x).", ""]
+    step_traffic = sum(per_k.get(k, 0.0) for k in step_names)
+    traffic = sum(per_k.get(k, 0.0) for k in attn_names)
+    out += ["", f"Decode-step call: {step_traffic / 1e6:.2f} MB of HBM traffic vs "
+                f"{alg['step'] / 1e6:.2f} MB algorithmic ({step_traffic / alg['step']:.3f}x).",
+            f"Decode-attention call alone: {traffic / 1e6:.2f} MB of HBM traffic vs "
+            f"{alg['attention'] / 1e6:.2f} MB algorithmic ({traffic / alg['attention']:.3f}x).", ""]
 
     util = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in _csv_rows(os.path.join(prof_dir, "util"), "counter_collection.csv"):
@@ -271,7 +293,7 @@ def summarize(prof_dir, workload, commands):
                 "| kernel | cycles | VALU busy | MFMA busy | VALU instr / wave | LDS bank conflicts |",
                 "|---|---|---|---|---|---|"]
         for k in sorted(util):
-            if not k.startswith("attn_"):
+            if not k.startswith(("attn_", "decode_step")):
                 continue
             m = {c: _median(v) for c, v in util[k].items()}
             cyc = m.get("GRBM_GUI_ACTIVE", float("nan")) / 8
@@ -282,8 +304,9 @@ def summarize(prof_dir, workload, commands):
         out.append("")
     print("\n".join(out))
 
-    entry = {"kernel_sources_sha": kernel_sources_sha(), "attn_bytes_per_launch": round(traffic),
-             "fetch_factor": f_fac, "write_factor": w_fac, "attn_us_trace": attn_us}
+    entry = {"kernel_sources_sha": kernel_sources_sha(), "step_bytes_per_launch": round(step_traffic),
+             "attn_bytes_per_launch": round(traffic), "fetch_factor": f_fac, "write_factor": w_fac,
+             "step_us_trace": step_us, "attn_us_trace": attn_us}
     try:
         with open(TRAFFIC_FILE) as f:
             allt = json.load(f)
@@ -358,12 +381,15 @@ def main():
                                f"bs={s.block_size} {s.kv_dtype}",
                    "batch": s.num_seqs, "q_tokens_per_seq": s.q_tokens, "context": int(w.max_seq_len - s.q_tokens),
                    "layers_rotated": head["layers_rotated"], "plan": head["plan"]},
-        "roofline": {"bound": "hbm", "achieved": head["attn_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": head["attn_GBs"] / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "kvd_decode_attention (split-K attention + combine)",
-                     "algorithmic_bytes_per_launch": head["attn_bytes"], "avg_launch_ms": head["attn_ms"]},
-        "step_GBs": head["step_GBs"],
-        "attn_tokens_per_s": head["attn_tokens_per_s"],
+        "roofline": {"bound": "hbm", "achieved": head["step_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": head["step_GBs"] / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "kvd_decode_step (fused RoPE + append + split-K attention kernel, "
+                               "then the split combine)",
+                     "algorithmic_bytes_per_launch": head["step_bytes"], "avg_launch_ms": head["step_ms"]},
+        "two_call_step_ms": head["two_call_step_ms"],
+        "attention_call": {"ms": head["attn_ms"], "GBs": head["attn_GBs"],
+                           "frac": head["attn_frac_of_peak"], "algorithmic_bytes": head["attn_bytes"],
+                           "tokens_per_s": head["attn_tokens_per_s"]},
         "cpu_baseline": cpu,
         "other_workloads": extra,
     }

@@ -177,6 +177,32 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv *kv, const float *q_rot, floa
                                 float softmax_scale, const kvd_attn_options *opt,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The whole decode step in one call: kvd_rope_append_kv followed by
+ * kvd_decode_attention_ex (generate.rs `step_gpu`: RoPE of the new q/k at the
+ * token's position, the append, then `mha_decode_t` over the cache; the
+ * Ferrum Infer README counts launches saved by fusing the steps of a decode).
+ *
+ *   q, k, v, rope_base, layout   as for kvd_rope_append_kv (q is NOT rotated
+ *                                in place).
+ *   q_rot   fp32 [B][T][Hq][D] receives the rotated queries, or NULL if the
+ *           caller does not want them.
+ *   out, softmax_scale, opt, workspace, workspace_bytes
+ *           as for kvd_decode_attention_ex (same workspace size).
+ *
+ * Results (out, q_rot, the cache) are bitwise those of the two calls in a
+ * row with the same plan.  When the plan uses the matrix-core kernel, one
+ * kernel does all of it (plus the split combine when there are several
+ * splits): each workgroup rotates its own query rows, and the workgroup whose
+ * key range holds the new tokens stores their K/V rows and uses them directly.
+ * Otherwise the RoPE/append kernel runs first and, if q_rot is NULL, `out`
+ * holds the rotated queries in between.
+ */
+int32_t kvd_decode_step(const kvd_paged_kv *kv, const float *q, const float *k, const float *v,
+                        float *q_rot, float *out, double rope_base, int32_t layout,
+                        float softmax_scale, const kvd_attn_options *opt, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kvd_status_string(int32_t status);
 

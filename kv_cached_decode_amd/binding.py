@@ -25,7 +25,8 @@ KVD_KERNEL_AUTO, KVD_KERNEL_VALU, KVD_KERNEL_MFMA = 0, 1, 2
 EXPORTED = [
     "kvd_rope_append_kv", "kvd_decode_attention", "kvd_decode_attention_ex",
     "kvd_decode_attention_workspace_size", "kvd_decode_attention_workspace_size_ex",
-    "kvd_decode_attention_plan", "kvd_status_string", "kvd_last_error", "kvd_abi_version",
+    "kvd_decode_attention_plan", "kvd_decode_step", "kvd_status_string", "kvd_last_error",
+    "kvd_abi_version",
 ]
 
 
@@ -86,6 +87,9 @@ def lib():
         L.kvd_decode_attention_plan.argtypes = [KV, OPT, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                                 ctypes.POINTER(I32)]
         L.kvd_decode_attention_plan.restype = I32
+        L.kvd_decode_step.argtypes = [KV, P, P, P, P, P, ctypes.c_double, I32, ctypes.c_float, OPT,
+                                      P, SZ, P]
+        L.kvd_decode_step.restype = I32
         L.kvd_status_string.argtypes = [I32]
         L.kvd_status_string.restype = ctypes.c_char_p
         L.kvd_last_error.argtypes = []
@@ -267,3 +271,32 @@ def decode_attention(kv: PagedKV, q_rot, out=None, softmax_scale=0.0, workspace_
                                          wbytes, _stream_handle(stream)),
            "kvd_decode_attention")
     return out
+
+
+def decode_step(kv: PagedKV, q, k, v, out=None, q_rot=None, want_q_rot=False, rope_base=10000.0,
+                layout=KVD_ROPE_HALF, softmax_scale=0.0, workspace_buf=None, num_splits=0,
+                kernel=KVD_KERNEL_AUTO, stream=None):
+    """kvd_decode_step: RoPE + append + decode attention in one call (one
+    kernel on matrix-core plans).  Returns out, or (out, q_rot) when q_rot is
+    given or want_q_rot is set."""
+    _need(q, "q", torch.float32, kv.q_shape())
+    _need(k, "k", torch.float32, kv.kv_shape())
+    _need(v, "v", torch.float32, kv.kv_shape())
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, kv.q_shape())
+    if q_rot is None and want_q_rot:
+        q_rot = torch.empty_like(q)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", torch.float32, kv.q_shape())
+    if workspace_buf is None:
+        workspace_buf = workspace(kv, num_splits, kernel)
+    wptr = workspace_buf.data_ptr() if workspace_buf is not None else None
+    wbytes = workspace_buf.numel() * workspace_buf.element_size() if workspace_buf is not None else 0
+    d = kv.struct()
+    _check(lib().kvd_decode_step(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 q_rot.data_ptr() if q_rot is not None else None, out.data_ptr(),
+                                 float(rope_base), int(layout), float(softmax_scale),
+                                 _opts(num_splits, kernel), wptr, wbytes, _stream_handle(stream)),
+           "kvd_decode_step")
+    return (out, q_rot) if q_rot is not None else out

@@ -24,12 +24,23 @@
 //       rows x 16 dims into 16 lanes x 4 keys), two reads per 32-key MFMA.
 //       O^T keeps the row in l%16, so the per-row rescale is lane-local.
 //
+// Fused decode step (FUSED): the kernel also does the RoPE + append step of
+// generate.rs `step_gpu` for its own rows and keys.  Every workgroup rotates
+// its query rows from the raw q (angles of the T new positions evaluated once
+// in fp64 into LDS, the same arithmetic as the stand-alone RoPE kernel); the
+// workgroup whose key range holds new tokens rotates and rounds their K/V
+// rows, stores them into the cache and substitutes them into its own tiles
+// from LDS, so it never waits for its own stores.  The result is bitwise the
+// RoPE/append kernel followed by the unfused attention with the same plan.
+//
 // Keys past the range are clamped to the range's last key for the loads and
 // masked to weight 0; keys past a draft token's position, or before its
 // sliding window, are masked the same way (causal within the draft).  Split
 // ranges start at the first key any query can see, so keys before every
 // window are not read.
+#include "bf16_round.h"
 #include "kvd_internal.h"
+#include "rope_math.h"
 
 namespace kvd {
 namespace {
@@ -47,6 +58,8 @@ constexpr int VT_BYTES = TILE * ROWB;    // one wave's V tile
 constexpr float M_EMPTY = -1e30f;
 constexpr int MAX_PIECE_BLOCKS = 2048;   // block ids staged in LDS at a time
 constexpr int LPT_MAX_SEQS = 256;        // batches ranked longest-first (one rank per thread)
+constexpr int MAX_T = 16;                // new tokens per sequence (rows <= 16)
+constexpr int HALF = D / 2;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -93,7 +106,8 @@ __device__ inline int lpt_rank_pick(int B, int z, const int* sm_len, int* sm_pic
     return *sm_pick;
 }
 
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+template <bool FUSED>
+__device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // the V tiles during the key loop, then the per-wave outputs
     constexpr int O_BYTES = WAVES * 16 * (D + 1) * 4;
     static_assert(O_BYTES <= WAVES * VT_BYTES, "output staging must fit in the V tiles");
@@ -102,6 +116,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     __shared__ float sm_m[WAVES][16];
     __shared__ float sm_l[WAVES][16];
     __shared__ int sm_pick;
+    // fused step: the rounded new K/V rows ([t][dim], bf16 bits), read by the
+    // key loop; before the loop the V-tile area holds, after the sequence
+    // lengths of the longest-first ranking, the cos/sin of the new positions'
+    // angles ([t][pair]) and the query rows being rotated
+    __shared__ __attribute__((aligned(16))) uint16_t sm_knew[FUSED ? MAX_T * D : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_vnew[FUSED ? MAX_T * D : 8];
+    double* const sm_cs = (double*)(sm_v + LPT_MAX_SEQS * 4);   // past the ranking's lengths
+    double* const sm_sn = sm_cs + MAX_T * HALF;
+    float* const sm_q = (float*)(sm_sn + MAX_T * HALF);
+    static_assert(LPT_MAX_SEQS * 4 + 2 * MAX_T * HALF * 8 + 16 * D * 4 <= WAVES * VT_BYTES,
+                  "fused scratch must fit in the V tiles");
     float (*sm_o)[16][D + 1] = (float (*)[16][D + 1])sm_v;
 
     const CacheView& c = a.c;
@@ -123,9 +148,34 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     // ranking keeps uniform batches in place -- and redone if it moves z.
     float xq[4][8];
     int tb = 0;
+    // fused step: this thread's first new-key pair (k pair, v pair) and the
+    // block it goes to, if the split holds new tokens
+    float kx = 0.0f, ky = 0.0f, vx = 0.0f, vy = 0.0f;
+    int kblk = 0;
     auto split_begin = [&](int LL) { return range_start(c, LL) + split * a.split_keys; };
+    auto new_pair = [&](int bb, int LL, int idx, int& ia, int& ic, size_t& src) {
+        const int n0 = max(LL - c.T, split_begin(LL));
+        const int t = n0 + idx / HALF - (LL - c.T);
+        rope_pair(idx % HALF, HALF, a.interleaved, ia, ic);
+        src = (((size_t)bb * c.T + t) * c.Hkv + kvh) * D;
+    };
     auto load_seq = [&](int bb, int LL) {
         const int key_begin = split_begin(LL);
+        if constexpr (FUSED) {
+            const int n0 = max(LL - c.T, key_begin);
+            const int n1 = min(LL, key_begin + a.split_keys);
+            if ((int)threadIdx.x < (n1 - n0) * HALF) {
+                int ia, ic;
+                size_t src;
+                new_pair(bb, LL, threadIdx.x, ia, ic, src);
+                const int i = threadIdx.x % HALF;
+                kx = a.k_new[src + ia];
+                ky = a.k_new[src + ic];
+                vx = a.v_new[src + 2 * i];
+                vy = a.v_new[src + 2 * i + 1];
+                kblk = c.table[(size_t)bb * c.max_blocks + ((n0 + (int)threadIdx.x / HALF) >> c.log2_bs)];
+            }
+        }
         const float* qp = a.q + (((size_t)bb * c.T + t_row) * c.Hq + h_row) * D;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -141,6 +191,22 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
             if ((int)threadIdx.x < nblk) tb = c.table[(size_t)bb * c.max_blocks + blk0 + threadIdx.x];
         }
     };
+    // Without a window a split's first key does not depend on the sequence
+    // length, so each lane fetches the block id of one key of its wave's
+    // first tile (lanes 32..63 repeat 0..31) together with the length: if
+    // the ranking below keeps this workgroup on sequence z, the first tile
+    // is issued from these ids, one memory round trip sooner.  The read stays
+    // inside the table row.
+    const int spec_base = split * a.split_keys + wave * TILE;
+    int spec_blk = 0;
+    // fused step: the frequency of this thread's rotation pair (pair
+    // threadIdx.x % HALF in every round of the angle loop)
+    const double theta = FUSED ? a.theta.v[threadIdx.x % HALF] : 0.0;
+    if (c.window == 0) {
+        const long long skey = (long long)spec_base + (lane & 31);
+        if (skey < ((long long)c.max_blocks << c.log2_bs))
+            spec_blk = c.table[(size_t)z * c.max_blocks + (int)(skey >> c.log2_bs)];
+    }
     int b = z;
     int L = c.seq_lens[z];
     load_seq(z, L);
@@ -162,17 +228,106 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int lo = c.window > 0 ? vis - c.window + 1 : 0;  // first key it sees
 
     // Q^T operand for row n16: dims 32*kk + 8*j .. +8, scaled into log2 units
-    // and split into bf16 hi + lo.
+    // and split into bf16 hi + lo.  Set up while the first tile's loads are
+    // in flight.
     bf16x8 qhi[4], qlo[4];
+    auto prepare_q = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = row_ok ? xq[kk][e] * a.scale_log2 : 0.0f;
-            const __bf16 hi = (__bf16)v;
-            qhi[kk][e] = hi;
-            qlo[kk][e] = (__bf16)(v - (float)hi);
+            for (int e = 0; e < 8; ++e) {
+                const float v = row_ok ? xq[kk][e] * a.scale_log2 : 0.0f;
+                const __bf16 hi = (__bf16)v;
+                qhi[kk][e] = hi;
+                qlo[kk][e] = (__bf16)(v - (float)hi);
+            }
+    };
+
+    // Fused step: the angles of the T new positions (once per workgroup, into
+    // LDS); the query rows rotated one pair per thread (rounded to fp32, as
+    // q_rot); the new K/V rows that fall in this split rotated, rounded to
+    // bf16, stored into the cache and kept in LDS for the tiles.
+    const int new0 = L - c.T;           // first new token's key index
+    auto fused_angles = [&]() {
+        static_assert(256 % HALF == 0, "a thread keeps its pair in every round");
+        for (int idx = threadIdx.x; idx < c.T * HALF; idx += blockDim.x)
+            rope_angle(theta, new0 + idx / HALF, sm_cs[idx], sm_sn[idx]);
+    };
+    auto fused_rotate_q = [&]() {
+        // this lane's raw slice of its row into LDS (every wave holds the
+        // same rows; wave 0 stores them), then one pair per thread, then each
+        // lane takes its rotated slice back (rotated per lane, the sixteen
+        // pairs' fp64 temporaries would not fit beside the first loads)
+        if (wave == 0 && row_ok) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                float* qs = sm_q + row * D + 32 * kk + 8 * j;
+                *(float4*)qs = make_float4(xq[kk][0], xq[kk][1], xq[kk][2], xq[kk][3]);
+                *(float4*)(qs + 4) = make_float4(xq[kk][4], xq[kk][5], xq[kk][6], xq[kk][7]);
+            }
         }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < a.rows * HALF; idx += blockDim.x) {
+            const int r = idx / HALF, i = idx % HALF, t = r / c.g;
+            int ia, ic;
+            rope_pair(i, HALF, a.interleaved, ia, ic);
+            double xr, yr;
+            rope_rotate(sm_q[r * D + ia], sm_q[r * D + ic], sm_cs[t * HALF + i], sm_sn[t * HALF + i], xr, yr);
+            const float x1 = (float)xr, y1 = (float)yr;
+            sm_q[r * D + ia] = x1;
+            sm_q[r * D + ic] = y1;
+            if (a.q_rot && split == 0) {
+                float* qr = a.q_rot + (((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g)) * D;
+                qr[ia] = x1;
+                qr[ic] = y1;
+            }
+        }
+        __syncthreads();
+        if (row_ok) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float4 x0 = *(const float4*)(sm_q + row * D + 32 * kk + 8 * j);
+                const float4 x1 = *(const float4*)(sm_q + row * D + 32 * kk + 8 * j + 4);
+                xq[kk][0] = x0.x; xq[kk][1] = x0.y; xq[kk][2] = x0.z; xq[kk][3] = x0.w;
+                xq[kk][4] = x1.x; xq[kk][5] = x1.y; xq[kk][6] = x1.z; xq[kk][7] = x1.w;
+            }
+        }
+    };
+    auto fused_append = [&]() {
+        // new keys n0 .. key_end-1 of this split (none unless it holds the
+        // tail); the first pair of each thread, and its block id, were loaded
+        // with q
+        const int n0 = max(new0, key_begin);
+        if (key_end <= n0) return;
+        uint16_t* kc = (uint16_t*)c.k;
+        uint16_t* vc = (uint16_t*)c.v;
+        for (int idx = threadIdx.x; idx < (key_end - n0) * HALF; idx += blockDim.x) {
+            const int key = n0 + idx / HALF, i = idx % HALF, t = key - new0;
+            int ia, ic;
+            size_t src;
+            new_pair(b, L, idx, ia, ic, src);
+            if (idx >= (int)blockDim.x) {
+                kx = a.k_new[src + ia];
+                ky = a.k_new[src + ic];
+                vx = a.v_new[src + 2 * i];
+                vy = a.v_new[src + 2 * i + 1];
+                kblk = c.table[(size_t)b * c.max_blocks + (key >> c.log2_bs)];
+            }
+            double xr, yr;
+            rope_rotate(kx, ky, sm_cs[t * HALF + i], sm_sn[t * HALF + i], xr, yr);
+            const uint16_t k0 = bf16_from_f64(xr), k1 = bf16_from_f64(yr);
+            const uint16_t v0 = bf16_from_f32(vx), v1 = bf16_from_f32(vy);
+            const size_t dst = ((((size_t)kblk * c.Hkv + kvh) << c.log2_bs) + (key & ((1 << c.log2_bs) - 1))) * D;
+            kc[dst + ia] = k0;
+            kc[dst + ic] = k1;
+            vc[dst + 2 * i] = v0;
+            vc[dst + 2 * i + 1] = v1;
+            sm_knew[t * D + ia] = k0;
+            sm_knew[t * D + ic] = k1;
+            sm_vnew[t * D + 2 * i] = v0;
+            sm_vnew[t * D + 2 * i + 1] = v1;
+        }
+    };
 
     const char* kbase = (const char*)c.k;
     const char* vbase = (const char*)c.v;
@@ -183,6 +338,45 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     f32x4 o[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    // K operands: tile h (16 keys), step kk: lane l reads key l%16, bytes
+    // [64*kk + 16*j, +16).  V rows: load i reads key 4*i + j, chunk n16.
+    // Keys past the piece end re-read its last key (weight 0 below).
+    // blk_of(key) gives the block id of a key of the tile.
+    u32x4 kf[8], vf[8];
+    auto issue = [&](int base, int pend, auto&& blk_of) {
+        auto row = [&](const char* basep, int key) -> const char* {
+            const size_t slot = (((size_t)blk_of(key) * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
+            return basep + slot * (D * 2);
+        };
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const char* kr = row(kbase, min(base + 16 * h + n16, pend - 1));
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kf[4 * h + kk] = __builtin_nontemporal_load((const u32x4*)(kr + 64 * kk + 16 * j));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const char* vr = row(vbase, min(base + 4 * i + j, pend - 1));
+            vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
+        }
+    };
+    const int first_p1 = (int)min((long long)key_end,
+                                  ((long long)(key_begin >> c.log2_bs) + MAX_PIECE_BLOCKS) << c.log2_bs);
+    // The fused step's work needs the sequence's length but not its block
+    // ids: it runs while the block-table loads are in flight, before the
+    // first tile is issued (whose registers its fp64 work would compete
+    // with) and before the first piece (whose barriers also publish the new
+    // K/V rows in LDS).
+    if constexpr (FUSED) {
+        fused_angles();
+        __syncthreads();
+        fused_rotate_q();
+        fused_append();
+    }
+    const bool spec = c.window == 0 && b == z && spec_base < first_p1;
+    if (spec) issue(spec_base, first_p1, [&](int key) { return __shfl(spec_blk, key - spec_base); });
 
     // pieces of at most MAX_PIECE_BLOCKS cache blocks (block ids in LDS)
     for (int p0 = key_begin; p0 < key_end;) {
@@ -200,38 +394,36 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         }
         __syncthreads();
 
-        auto row_addr = [&](const char* base, int key) -> const char* {
-            const int blk = sm_blk[(key >> c.log2_bs) - blk0];
-            const size_t slot = (((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
-            return base + slot * (D * 2);
-        };
-        // K operands: tile h (16 keys), step kk: lane l reads key l%16,
-        // bytes [64*kk + 16*j, +16).  V rows: load i reads key 4*i + j, chunk
-        // n16.  Keys past the piece re-read its last key (weight 0 below).
-        auto issue = [&](int base, u32x4 (&kf)[8], u32x4 (&vf)[8]) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const char* kr = row_addr(kbase, min(base + 16 * h + n16, p1 - 1));
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    kf[4 * h + kk] = __builtin_nontemporal_load((const u32x4*)(kr + 64 * kk + 16 * j));
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const char* vr = row_addr(vbase, min(base + 4 * i + j, p1 - 1));
-                vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
-            }
-        };
+        auto staged = [&](int key) { return sm_blk[(key >> c.log2_bs) - blk0]; };
 
         // One buffer of K/V registers per wave: the V rows go to LDS and the
         // K rows into the score MFMAs first, then the registers take the next
         // tile's loads, which stay in flight through the softmax and P.V of
         // this tile (and behind the other wave on the SIMD).
-        u32x4 kf[8], vf[8];
         constexpr int STRIDE = WAVES * TILE;
         int base = p0 + wave * TILE;
-        if (base < p1) issue(base, kf, vf);
+        if (base < p1 && !(spec && p0 == key_begin)) issue(base, p1, staged);
+        if (p0 == key_begin) prepare_q();
         for (; base < p1; base += STRIDE) {
+            if constexpr (FUSED) {
+                // rows of new tokens (also where a clamped lane re-reads one)
+                // come from LDS, whatever the loads returned
+                if (min(base + TILE, p1) - 1 >= new0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int key = min(base + 16 * h + n16, p1 - 1);
+                        if (key >= new0)
+#pragma unroll
+                            for (int kk = 0; kk < 4; ++kk)
+                                kf[4 * h + kk] = *(const u32x4*)(sm_knew + (key - new0) * D + 32 * kk + 8 * j);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int key = min(base + 4 * i + j, p1 - 1);
+                        if (key >= new0) vf[i] = *(const u32x4*)(sm_vnew + (key - new0) * D + 8 * n16);
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (4 * i + j) * ROWB + 16 * n16) = vf[i];
 
@@ -248,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
                 }
                 s[h] = acc;
             }
-            if (base + STRIDE < p1) issue(base + STRIDE, kf, vf);
+            if (base + STRIDE < p1) issue(base + STRIDE, p1, staged);
 
             // mask, running max, weights
             float mx = m;
@@ -335,6 +527,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) { attn_mfma_body<false>(a); }
+
+// the fused decode step (its own name, so that profiles tell the two apart)
+__global__ __launch_bounds__(256, 2) void decode_step_mfma_kernel(AttnArgs a) { attn_mfma_body<true>(a); }
+
 }  // namespace
 
 bool mfma_supported(int D_, int kv_bf16, int rows) { return D_ == D && kv_bf16 && rows >= 1 && rows <= 16; }
@@ -343,7 +540,10 @@ int mfma_step_keys() { return WAVES * TILE; }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
     dim3 grid(a.num_splits, a.c.Hkv, a.c.B);
-    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), 0, s, a);
+    if (a.fused)
+        hipLaunchKernelGGL(decode_step_mfma_kernel, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

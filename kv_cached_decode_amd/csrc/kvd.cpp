@@ -223,11 +223,147 @@ Carve carve(const kvd_paged_kv* kv, const Plan& p) {
 
 size_t workspace_for(const kvd_paged_kv* kv, const Plan& p) { return carve(kv, p).total; }
 
+// RoPE frequencies theta_i = base^(-2i/D), i < D/2, in fp64 (the last table
+// is kept per thread: a decode loop asks for the same one every step).
+void fill_theta(kvd::RopeTheta* t, double base, int D) {
+    thread_local double last_base = 0.0;
+    thread_local int last_D = 0;
+    thread_local kvd::RopeTheta last;
+    if (base != last_base || D != last_D) {
+        for (int i = 0; i < 128; ++i)
+            last.v[i] = i < D / 2 ? std::pow(base, -2.0 * (double)i / (double)D) : 0.0;
+        last_base = base;
+        last_D = D;
+    }
+    *t = last;
+}
+
+// Arguments of the RoPE + append step (q_rot may be null: the fused step
+// makes it optional).
+int32_t check_rope(const float* q, const float* k, const float* v, const float* q_rot,
+                   double rope_base, int32_t layout) {
+    if (!q || !k || !v) return fail(KVD_ERR_NULL, "q, k and v must be non-NULL");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)q_rot) & 3)
+        return fail(KVD_ERR_SHAPE, "q, k, v, q_rot must be 4-byte aligned");
+    if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+        return fail(KVD_ERR_SHAPE, "rope_base must be finite and > 0");
+    if (layout != KVD_ROPE_HALF && layout != KVD_ROPE_INTERLEAVED)
+        return fail(KVD_ERR_UNSUPPORTED, "rope layout = %d", layout);
+    return KVD_OK;
+}
+
+int32_t rope_append(const kvd_paged_kv* kv, const float* q, const float* k, const float* v,
+                    float* q_rot, double rope_base, int32_t layout, void* stream) {
+    kvd::RopeAppendArgs a;
+    a.c = view_of(kv);
+    a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
+    a.interleaved = layout == KVD_ROPE_INTERLEAVED;
+    fill_theta(&a.theta, rope_base, kv->head_dim);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_rot = q_rot;
+    hipError_t e = kvd::launch_rope_append(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "rope_append_kv launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Inputs of the fused decode step (RoPE + append inside the attention kernel).
+struct FuseIn {
+    const float* k;
+    const float* v;
+    float* q_rot;         // may be null
+    double rope_base;
+    int32_t layout;
+};
+
+// Decode attention; with `fuse`, q_rot is the raw q and the matrix-core
+// kernel also rotates it and appends the new K/V rows.  The descriptor has
+// been checked and num_seqs > 0.
+int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float softmax_scale,
+                  const kvd_attn_options* opt, void* workspace, size_t workspace_bytes, void* stream,
+                  const FuseIn* fuse) {
+    int32_t st;
+    if (!q_rot || !out) return fail(KVD_ERR_NULL, "q and out must be non-NULL");
+    if (((uintptr_t)q_rot | (uintptr_t)out) & 3)
+        return fail(KVD_ERR_SHAPE, "q and out must be 4-byte aligned");
+    if (!std::isfinite(softmax_scale))
+        return fail(KVD_ERR_SHAPE, "softmax_scale must be finite");
+    Plan p;
+    st = make_plan(kv, opt, &p);
+    if (st != KVD_OK) return st;
+    const size_t need = workspace_for(kv, p);
+    if (need > 0) {
+        if (!workspace) return fail(KVD_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+        if (workspace_bytes < need)
+            return fail(KVD_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+        if ((uintptr_t)workspace & 255) return fail(KVD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    const double scale = softmax_scale != 0.0f ? (double)softmax_scale : 1.0 / std::sqrt((double)kv->head_dim);
+    kvd::AttnArgs a;
+    a.c = view_of(kv);
+    a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
+    a.num_splits = p.splits;
+    a.split_keys = p.split_keys;
+    a.rows = p.rows;
+    a.row_tile = p.row_tile;
+    a.scale_log2 = (float)(scale * 1.4426950408889634);
+    a.q = q_rot;
+    a.out = out;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    a.fused = fuse != nullptr;
+    a.interleaved = fuse && fuse->layout == KVD_ROPE_INTERLEAVED;
+    if (fuse) fill_theta(&a.theta, fuse->rope_base, kv->head_dim);
+    a.k_new = fuse ? fuse->k : nullptr;
+    a.v_new = fuse ? fuse->v : nullptr;
+    a.q_rot = fuse ? fuse->q_rot : nullptr;
+    if (need > 0) {
+        const Carve cv = carve(kv, p);
+        a.part_o = (float*)((char*)workspace + cv.o);
+        a.part_ml = (float*)((char*)workspace + cv.ml);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s) : kvd::launch_attn_valu(a, s);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "decode attention launch: %s", hipGetErrorString(e));
+    if (p.splits > 1) {
+        e = kvd::launch_attn_combine(a, s);
+        if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t kvd_abi_version(void) { return 2; }
+
+int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, const float* v,
+                        float* q_rot, float* out, double rope_base, int32_t layout,
+                        float softmax_scale, const kvd_attn_options* opt, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (kv->num_seqs == 0) return ok();
+    if (!out) return fail(KVD_ERR_NULL, "out must be non-NULL");
+    st = check_rope(q, k, v, q_rot, rope_base, layout);
+    if (st != KVD_OK) return st;
+    Plan p;
+    st = make_plan(kv, opt, &p);
+    if (st != KVD_OK) return st;
+    if (p.kernel == KVD_KERNEL_MFMA) {
+        const FuseIn f{k, v, q_rot, rope_base, layout};
+        return attention(kv, q, out, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
+    }
+    // vector-ALU plans: the two kernels in a row; `out` holds the rotated
+    // queries when the caller wants none back (each output row is written
+    // only after its query row has been read)
+    float* qr = q_rot ? q_rot : out;
+    st = rope_append(kv, q, k, v, qr, rope_base, layout, stream);
+    if (st != KVD_OK) return st;
+    return attention(kv, qr, out, softmax_scale, opt, workspace, workspace_bytes, stream, nullptr);
+}
 
 const char* kvd_status_string(int32_t s) {
     switch (s) {
@@ -248,25 +384,10 @@ int32_t kvd_rope_append_kv(const kvd_paged_kv* kv, const float* q, const float* 
     int32_t st = check_desc(kv);
     if (st != KVD_OK) return st;
     if (kv->num_seqs == 0) return ok();
-    if (!q || !k || !v || !q_rot) return fail(KVD_ERR_NULL, "q, k, v and q_rot must be non-NULL");
-    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)q_rot) & 3)
-        return fail(KVD_ERR_SHAPE, "q, k, v, q_rot must be 4-byte aligned");
-    if (!(rope_base > 0.0) || !std::isfinite(rope_base))
-        return fail(KVD_ERR_SHAPE, "rope_base must be finite and > 0");
-    if (layout != KVD_ROPE_HALF && layout != KVD_ROPE_INTERLEAVED)
-        return fail(KVD_ERR_UNSUPPORTED, "rope layout = %d", layout);
-    kvd::RopeAppendArgs a;
-    a.c = view_of(kv);
-    a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
-    a.interleaved = layout == KVD_ROPE_INTERLEAVED;
-    a.base = rope_base;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.q_rot = q_rot;
-    hipError_t e = kvd::launch_rope_append(a, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "rope_append_kv launch: %s", hipGetErrorString(e));
-    return ok();
+    if (!q_rot) return fail(KVD_ERR_NULL, "q_rot must be non-NULL");
+    st = check_rope(q, k, v, q_rot, rope_base, layout);
+    if (st != KVD_OK) return st;
+    return rope_append(kv, q, k, v, q_rot, rope_base, layout, stream);
 }
 
 size_t kvd_decode_attention_workspace_size_ex(const kvd_paged_kv* kv, const kvd_attn_options* opt) {
@@ -306,47 +427,7 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv* kv, const float* q_rot, floa
     int32_t st = check_desc(kv);
     if (st != KVD_OK) return st;
     if (kv->num_seqs == 0) return ok();
-    if (!q_rot || !out) return fail(KVD_ERR_NULL, "q_rot and out must be non-NULL");
-    if (((uintptr_t)q_rot | (uintptr_t)out) & 3)
-        return fail(KVD_ERR_SHAPE, "q_rot and out must be 4-byte aligned");
-    if (!std::isfinite(softmax_scale))
-        return fail(KVD_ERR_SHAPE, "softmax_scale must be finite");
-    Plan p;
-    st = make_plan(kv, opt, &p);
-    if (st != KVD_OK) return st;
-    const size_t need = workspace_for(kv, p);
-    if (need > 0) {
-        if (!workspace) return fail(KVD_ERR_WORKSPACE, "workspace of %zu bytes required", need);
-        if (workspace_bytes < need)
-            return fail(KVD_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-        if ((uintptr_t)workspace & 255) return fail(KVD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    }
-    const double scale = softmax_scale != 0.0f ? (double)softmax_scale : 1.0 / std::sqrt((double)kv->head_dim);
-    kvd::AttnArgs a;
-    a.c = view_of(kv);
-    a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
-    a.num_splits = p.splits;
-    a.split_keys = p.split_keys;
-    a.rows = p.rows;
-    a.row_tile = p.row_tile;
-    a.scale_log2 = (float)(scale * 1.4426950408889634);
-    a.q = q_rot;
-    a.out = out;
-    a.part_o = nullptr;
-    a.part_ml = nullptr;
-    if (need > 0) {
-        const Carve cv = carve(kv, p);
-        a.part_o = (float*)((char*)workspace + cv.o);
-        a.part_ml = (float*)((char*)workspace + cv.ml);
-    }
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s) : kvd::launch_attn_valu(a, s);
-    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "decode attention launch: %s", hipGetErrorString(e));
-    if (p.splits > 1) {
-        e = kvd::launch_attn_combine(a, s);
-        if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
-    }
-    return ok();
+    return attention(kv, q_rot, out, softmax_scale, opt, workspace, workspace_bytes, stream, nullptr);
 }
 
 int32_t kvd_decode_attention(const kvd_paged_kv* kv, const float* q_rot, float* out,

@@ -27,11 +27,16 @@ __device__ inline int range_start(const CacheView& c, int L) {
     return c.window > 0 ? max(0, L - c.T - c.window + 1) : 0;
 }
 
+// theta_i = rope_base^(-2i/D) for i < D/2, evaluated on the host.
+struct RopeTheta {
+    double v[128];
+};
+
 struct RopeAppendArgs {
     CacheView c;
     int32_t kv_bf16;
     int32_t interleaved;
-    double base;
+    RopeTheta theta;
     const float* q;
     const float* k;
     const float* v;
@@ -52,6 +57,15 @@ struct AttnArgs {
     float* out;             // [B][T][Hq][D] (written directly when S == 1)
     float* part_o;          // [B][T][Hq][S][D]   unnormalised partial outputs
     float* part_ml;         // [B][T][Hq][S][2]   (running max in log2 units, sum)
+    // Fused decode step (matrix-core kernel only): q holds the raw queries;
+    // the kernel rotates them, appends the new K/V rows of its split to the
+    // cache and writes the rotated queries to q_rot when that is non-null.
+    int32_t fused;
+    int32_t interleaved;
+    RopeTheta theta;
+    const float* k_new;     // [B][T][Hkv][D] new keys before RoPE
+    const float* v_new;     // [B][T][Hkv][D] new values
+    float* q_rot;           // [B][T][Hq][D] or null
 };
 
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);

@@ -4,28 +4,19 @@
 // per-item positions, paged KV through a block table).
 //
 // One workgroup per new token (b, t).  The token's position is
-// seq_lens[b] - T + t.  The D/2 rotation angles pos * base^(-2i/D) are
-// evaluated once per token in fp64 and shared through LDS; every head's pair
+// seq_lens[b] - T + t.  The D/2 rotation angles pos * theta_i (theta_i =
+// base^(-2i/D) from the host) are evaluated once per token in fp64 and shared
+// through LDS; every head's pair
 // is then rotated in fp64 and rounded once: to fp32 for q_rot and an fp32
 // cache, to bf16 (round to nearest even) for a bf16 cache.  The volume is
 // tiny (B*T*(Hq + 2*Hkv)*D elements), so the kernel is latency-bound: it
 // spreads a token's heads over several workgroups, one pair per thread.
 #include "bf16_round.h"
 #include "kvd_internal.h"
+#include "rope_math.h"
 
 namespace kvd {
 namespace {
-
-__device__ inline void pair_of(int i, int half, int interleaved, int& ia, int& ic) {
-    if (interleaved) { ia = 2 * i; ic = 2 * i + 1; }
-    else             { ia = i;     ic = i + half; }
-}
-
-__device__ inline void rotate(double x, double y, double c, double s, double& xr, double& yr) {
-#pragma clang fp contract(off)
-    xr = x * c - y * s;
-    yr = x * s + y * c;
-}
 
 // Heads of one token are numbered q heads, then k heads, then v heads; a
 // workgroup rotates/stores HEADS_PER_WG of them (D/2 pair slots each), so
@@ -43,7 +34,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const int i = (int)threadIdx.x % half;
     const bool active = (int)threadIdx.x < heads_per_wg * half && head < c.Hq + 2 * c.Hkv;
     int ia, ic;
-    pair_of(i, half, a.interleaved, ia, ic);
+    rope_pair(i, half, a.interleaved, ia, ic);
 
     // This thread's inputs first (they do not depend on the angles), so their
     // latency overlaps the fp64 angle evaluation below.
@@ -66,12 +57,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const int pos = c.seq_lens[b] - c.T + t;
     const int blk = c.table[(size_t)b * c.max_blocks + (pos >> c.log2_bs)];
 
-    for (int p = threadIdx.x; p < half; p += blockDim.x) {
-        double theta = pow(a.base, -2.0 * (double)p / (double)D);
-        double phi = (double)pos * theta;
-        cs[p] = cos(phi);
-        sn[p] = sin(phi);
-    }
+    for (int p = threadIdx.x; p < half; p += blockDim.x) rope_angle(a.theta.v[p], pos, cs[p], sn[p]);
     __syncthreads();
     if (!active) return;
 
@@ -80,7 +66,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
         // written by this thread only.
         const size_t o = ((size_t)token * c.Hq + head) * D;
         double xr, yr;
-        rotate(x0, x1, cs[i], sn[i], xr, yr);
+        rope_rotate(x0, x1, cs[i], sn[i], xr, yr);
         a.q_rot[o + ia] = (float)xr;
         a.q_rot[o + ic] = (float)yr;
         return;
@@ -91,7 +77,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
         const int h = head - c.Hq;
         const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
         double xr, yr;
-        rotate(x0, x1, cs[i], sn[i], xr, yr);
+        rope_rotate(x0, x1, cs[i], sn[i], xr, yr);
         if (a.kv_bf16) {
             uint16_t* kc = (uint16_t*)c.k;
             kc[dst + ia] = bf16_from_f64(xr);

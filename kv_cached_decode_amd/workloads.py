@@ -137,8 +137,10 @@ class Workload:
         table = int(sum((int(L) + s.block_size - 1) // s.block_size for L in self.seq_lens)) * 4
         attn = kv_read + qo + table + B * 4
         rope_append = B * T * (Hq * D * 4 * 2 + 2 * Hkv * D * (4 + esz)) + B * 4 + B * T * 4
-        return {"kv_read": kv_read, "attention": attn, "rope_append": rope_append,
-                "step": attn + rope_append}
+        # the whole step: the cache read, q in, out, the new k/v in and their
+        # append, the block table and seq_lens (no intermediate q_rot)
+        step = attn + B * T * 2 * Hkv * D * (4 + esz)
+        return {"kv_read": kv_read, "attention": attn, "rope_append": rope_append, "step": step}
 
 
 def _draw(rng, n, dist, dtype_out):

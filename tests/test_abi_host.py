@@ -84,6 +84,9 @@ def test_bad_descriptor_rejected_before_launch(kw, status):
     assert kb.last_error()
     st = L.kvd_rope_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 10000.0, 0, None)
     assert st == status, kb.last_error()
+    st = L.kvd_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 10000.0, 0, 0.0, None, ws,
+                           1 << 30, None)
+    assert st == status, kb.last_error()
     assert L.kvd_decode_attention_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
 
 
@@ -91,6 +94,8 @@ def test_null_descriptor():
     L = kb.lib()
     assert L.kvd_decode_attention(None, FAKE, FAKE, 0.0, None, 0, None) == kb.KVD_ERR_NULL
     assert L.kvd_rope_append_kv(None, FAKE, FAKE, FAKE, FAKE, 1e4, 0, None) == kb.KVD_ERR_NULL
+    assert L.kvd_decode_step(None, FAKE, FAKE, FAKE, None, FAKE, 1e4, 0, 0.0, None, None, 0,
+                             None) == kb.KVD_ERR_NULL
 
 
 def test_bad_call_arguments():
@@ -112,11 +117,37 @@ def test_bad_call_arguments():
                                      need, None) == kb.KVD_ERR_UNSUPPORTED
 
 
+def test_decode_step_bad_arguments():
+    """The fused step checks the union of the two calls' arguments; q_rot may
+    be NULL, out may not."""
+    L = kb.lib()
+    d = desc(max_blocks_per_seq=64, max_seq_len=1000)
+    need = L.kvd_decode_attention_workspace_size(ctypes.byref(d))
+
+    def step(q=FAKE, k=FAKE, v=FAKE, q_rot=None, out=FAKE, base=1e4, layout=0, scale=0.0, opt=None,
+             ws=FAKE, nbytes=need):
+        return L.kvd_decode_step(ctypes.byref(d), q, k, v, q_rot, out, base, layout, scale, opt, ws,
+                                 nbytes, None)
+
+    assert step(q=0) == kb.KVD_ERR_NULL
+    assert step(k=0) == kb.KVD_ERR_NULL
+    assert step(out=0) == kb.KVD_ERR_NULL
+    assert step(q_rot=FAKE + 2) == kb.KVD_ERR_SHAPE
+    assert step(base=0.0) == kb.KVD_ERR_SHAPE
+    assert step(layout=5) == kb.KVD_ERR_UNSUPPORTED
+    assert step(scale=float("inf")) == kb.KVD_ERR_SHAPE
+    assert step(ws=None, nbytes=0) == kb.KVD_ERR_WORKSPACE
+    assert step(nbytes=need - 1) == kb.KVD_ERR_WORKSPACE
+    assert step(opt=ctypes.byref(kb.KvdAttnOptions(0, 9))) == kb.KVD_ERR_UNSUPPORTED
+
+
 def test_empty_batch_is_a_noop():
     L = kb.lib()
     d = desc(num_seqs=0, k_cache=0, v_cache=0, block_table=0, seq_lens=0)
     assert L.kvd_decode_attention(ctypes.byref(d), 0, 0, 0.0, None, 0, None) == kb.KVD_OK
     assert L.kvd_rope_append_kv(ctypes.byref(d), 0, 0, 0, 0, 1e4, 0, None) == kb.KVD_OK
+    assert L.kvd_decode_step(ctypes.byref(d), 0, 0, 0, None, 0, 1e4, 0, 0.0, None, None, 0,
+                             None) == kb.KVD_OK
     assert L.kvd_decode_attention_workspace_size(ctypes.byref(d)) == 0
 
 
