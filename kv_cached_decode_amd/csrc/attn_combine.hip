@@ -5,9 +5,10 @@
 // the sum of 2^(score - m_s) over its keys and the matching unnormalised
 // weighted sum of V.  The row's result is
 //     M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
-// over the splits that hold keys of this sequence (split s exists when
-// range_start + s * split_keys < seq_lens[b]).  Splits whose keys the row cannot see carry
-// l_s = 0 and a very negative m_s, and drop out.
+// over all S splits: a split with no key of the sequence, or none the row
+// can see, carries l_s = 0, o_s = 0 and a very negative m_s, and drops out.
+// Nothing here depends on the sequence lengths, so the merge costs one
+// memory round trip.
 //
 // Fixed summation order, so results are bitwise reproducible.
 #include "kvd_internal.h"
@@ -76,10 +77,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     __shared__ float sm_red[2];
     const CacheView& c = a.c;
     const size_t qrow = blockIdx.x;                     // (b*T + t)*Hq + h
-    const int b = (int)(qrow / ((size_t)c.T * c.Hq));
-    const int L = c.seq_lens[b];
     const int S = a.num_splits;
-    const int n = min(S, (L - range_start(c, L) + a.split_keys - 1) / a.split_keys);
+    const int n = S;
     if (combine_small<8>(a, qrow, n)) return;
     const float* ml = a.part_ml + qrow * S * 2;
     const float* po = a.part_o + qrow * S * c.D;

@@ -222,7 +222,10 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         }
     }
     const int key_begin = split_begin(L);
-    if (key_begin >= L) return;         // empty split: the combine skips it
+    if (key_begin >= L) {               // empty split
+        write_empty_partials(a, b, kvh, split, 0, a.rows);
+        return;
+    }
     const int key_end = min(L, key_begin + a.split_keys);
     const int vis = row_ok ? L - c.T + t_row : L - 1;     // last key this row sees
     const int lo = c.window > 0 ? vis - c.window + 1 : 0;  // first key it sees

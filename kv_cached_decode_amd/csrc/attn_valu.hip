@@ -116,7 +116,10 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 
     const int L = c.seq_lens[b];
     const int key_begin = range_start(c, L) + split * a.split_keys;
-    if (key_begin >= L) return;               // empty split: the combine skips it
+    if (key_begin >= L) {                     // empty split
+        write_empty_partials(a, b, kvh, split, rtile * RT, RT);
+        return;
+    }
     const int key_end = min(L, key_begin + a.split_keys);
 
     // stage the block ids of [key_begin, key_end) in LDS

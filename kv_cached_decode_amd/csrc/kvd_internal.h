@@ -68,6 +68,25 @@ struct AttnArgs {
     float* q_rot;           // [B][T][Hq][D] or null
 };
 
+// A split that holds no key of its sequence leaves, for its rows, a partial
+// that drops out of the merge (running max -1e30, sum 0, output 0), so the
+// merge combines every split without reading the sequence lengths.
+__device__ inline void write_empty_partials(const AttnArgs& a, int b, int kvh, int split, int row0,
+                                            int nrows) {
+    if (a.num_splits == 1) return;
+    const CacheView& c = a.c;
+    const int D = c.D;
+    for (int idx = threadIdx.x; idx < nrows * (D + 2); idx += blockDim.x) {
+        const int r = row0 + idx / (D + 2), e = idx % (D + 2);
+        if (r >= a.rows) continue;
+        const int t = r / c.g;
+        const size_t qrow = ((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g);
+        const size_t part = qrow * a.num_splits + split;
+        if (e < D) a.part_o[part * D + e] = 0.0f;
+        else a.part_ml[part * 2 + (e - D)] = e == D ? -1e30f : 0.0f;
+    }
+}
+
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
