@@ -21,7 +21,15 @@
  *       s_j = scale * <q_rot, K_j>, j = j0 .. p, p = seq_lens[b] - T + t,
  *       j0 = 0, or max(0, p - window + 1) with a window,
  *       out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s),
+ *       lse = log sum_j exp(s_j),
  *       kv head of query head h = h / (Hq / Hkv).
+ *
+ *   Context-parallel shard (context parallelism, CP and DCP, is one of the
+ *   composable parallel modes on the ferrite page): the cache holds global
+ *   keys key_pos0 .. key_pos0 + seq_lens - 1 and the new tokens sit at
+ *   q_pos + t; the same sums run over the held keys only, so the shards'
+ *   (out, lse) pairs merge into the whole-cache result by
+ *       LSE = log sum_p exp(lse_p),  out = sum_p exp(lse_p - LSE) out_p.
  */
 #include "kvd_oracle.h"
 
@@ -132,7 +140,7 @@ static int check_cache(const oracle_cache *c)
         return 1;
     for (int32_t b = 0; b < c->num_seqs; ++b) {
         int64_t L = c->seq_lens[b];
-        if (L < c->q_tokens)
+        if (L < (c->q_pos ? 0 : c->q_tokens))
             return 1;
         int64_t nblk = (L + c->block_size - 1) / c->block_size;
         if (nblk > c->max_blocks_per_seq)
@@ -146,7 +154,18 @@ static int check_cache(const oracle_cache *c)
     return 0;
 }
 
-/* Flat element index of (key position pos of sequence b, kv head, dim 0). */
+/* Global position of new token 0 of sequence b, and of local key 0. */
+static int64_t q_pos0(const oracle_cache *c, int32_t b)
+{
+    return c->q_pos ? (int64_t)c->q_pos[b] : (int64_t)c->seq_lens[b] - c->q_tokens;
+}
+
+static int64_t key_pos0(const oracle_cache *c, int32_t b)
+{
+    return c->key_pos0 ? (int64_t)c->key_pos0[b] : 0;
+}
+
+/* Flat element index of (local key pos of sequence b, kv head, dim 0). */
 static size_t slot_index(const oracle_cache *c, int32_t b, int64_t pos,
                          int32_t kvh)
 {
@@ -195,7 +214,13 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
     }
     for (int32_t b = 0; b < B; ++b)
         for (int32_t t = 0; t < T; ++t) {
-            int64_t pos = (int64_t)c->seq_lens[b] - T + t;
+            int64_t pos = q_pos0(c, b) + t;              /* global: the rotation */
+            int64_t local = pos - key_pos0(c, b);        /* the cache slot */
+            if (local < 0 || local >= c->seq_lens[b]) {
+                free(x);
+                free(y);
+                return 1;
+            }
             for (int32_t h = 0; h < Hq; ++h) {
                 size_t o = (((size_t)b * T + t) * Hq + h) * D;
                 for (int32_t d = 0; d < D; ++d)
@@ -204,7 +229,7 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
             }
             for (int32_t h = 0; h < Hkv; ++h) {
                 size_t o = (((size_t)b * T + t) * Hkv + h) * D;
-                size_t s = slot_index(c, b, pos, h);
+                size_t s = slot_index(c, b, local, h);
                 for (int32_t d = 0; d < D; ++d)
                     x[d] = (double)k[o + d];
                 rope_one(x, y, D, pos, base, layout);
@@ -219,39 +244,53 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
     return 0;
 }
 
-/* One query row: q (D values) of sequence b against keys j0 .. n_vis-1 of kv
- * head kvh, j0 = 0 or the start of the sliding window.  Writes out[D], *lse
- * and *wsum. */
-static int attend_row(const oracle_cache *c, int32_t b, int32_t kvh,
-                      int64_t n_vis, const double *q, double scale,
-                      double *out, double *lse, double *wsum)
+/* One query row: q (D values) of sequence b at global position p, against
+ * the keys it sees: global 0 .. p, or p - window + 1 .. p, of those the cache
+ * holds (local keys i0 .. i1-1 below).  Writes out[D], *lse and *wsum; a row
+ * that sees no key gets out = 0, lse = -inf, wsum = 0. */
+static int attend_row(const oracle_cache *c, int32_t b, int32_t kvh, int64_t p,
+                      const double *q, double scale, double *out, double *lse,
+                      double *wsum)
 {
     const int32_t D = c->head_dim;
-    const int64_t j0 = (c->window > 0 && n_vis > c->window) ? n_vis - c->window : 0;
-    double *s = (double *)malloc(sizeof(double) * (size_t)n_vis);
+    const int64_t k0 = key_pos0(c, b);
+    int64_t g0 = (c->window > 0 && p + 1 > c->window) ? p + 1 - c->window : 0;
+    int64_t i0 = g0 - k0, i1 = p + 1 - k0;
+    if (i0 < 0)
+        i0 = 0;
+    if (i1 > c->seq_lens[b])
+        i1 = c->seq_lens[b];
+    for (int32_t d = 0; d < D; ++d)
+        out[d] = 0.0;
+    if (i1 <= i0) {
+        if (lse)
+            *lse = -INFINITY;
+        if (wsum)
+            *wsum = 0.0;
+        return 0;
+    }
+    double *s = (double *)malloc(sizeof(double) * (size_t)(i1 - i0));
     if (!s)
         return 2;
     double m = -INFINITY;
-    for (int64_t j = j0; j < n_vis; ++j) {
+    for (int64_t j = i0; j < i1; ++j) {
         size_t idx = slot_index(c, b, j, kvh);
         double dot = 0.0;
         for (int32_t d = 0; d < D; ++d)
             dot += q[d] * load(c, c->k_pool, idx + d);
-        s[j] = scale * dot;
-        if (s[j] > m)
-            m = s[j];
+        s[j - i0] = scale * dot;
+        if (s[j - i0] > m)
+            m = s[j - i0];
     }
     double denom = 0.0;
-    for (int64_t j = j0; j < n_vis; ++j) {
-        s[j] = exp(s[j] - m);   /* unnormalised weight */
-        denom += s[j];
+    for (int64_t j = i0; j < i1; ++j) {
+        s[j - i0] = exp(s[j - i0] - m);   /* unnormalised weight */
+        denom += s[j - i0];
     }
-    for (int32_t d = 0; d < D; ++d)
-        out[d] = 0.0;
     double total = 0.0;
-    for (int64_t j = j0; j < n_vis; ++j) {
+    for (int64_t j = i0; j < i1; ++j) {
         size_t idx = slot_index(c, b, j, kvh);
-        double w = s[j] / denom;
+        double w = s[j - i0] / denom;
         total += w;
         for (int32_t d = 0; d < D; ++d)
             out[d] += w * load(c, c->v_pool, idx + d);
@@ -283,9 +322,8 @@ int oracle_decode_attention_rows(const oracle_cache *c, const double *q_rot,
         int32_t h = (int32_t)(row % Hq);
         int32_t t = (int32_t)((row / Hq) % T);
         int32_t b = (int32_t)(row / ((int64_t)Hq * T));
-        int64_t n_vis = (int64_t)c->seq_lens[b] - T + t + 1;
-        err |= attend_row(c, b, h / g, n_vis, q_rot + (size_t)row * D, scale,
-                          out + (size_t)r * D, lse ? lse + r : NULL, NULL);
+        err |= attend_row(c, b, h / g, q_pos0(c, b) + t, q_rot + (size_t)row * D,
+                          scale, out + (size_t)r * D, lse ? lse + r : NULL, NULL);
     }
     return err;
 }
@@ -305,9 +343,8 @@ int oracle_decode_attention(const oracle_cache *c, const double *q_rot,
         int32_t h = (int32_t)(row % Hq);
         int32_t t = (int32_t)((row / Hq) % T);
         int32_t b = (int32_t)(row / ((int64_t)Hq * T));
-        int64_t n_vis = (int64_t)c->seq_lens[b] - T + t + 1;
-        err |= attend_row(c, b, h / g, n_vis, q_rot + (size_t)row * D, scale,
-                          out + (size_t)row * D, lse ? lse + row : NULL,
+        err |= attend_row(c, b, h / g, q_pos0(c, b) + t, q_rot + (size_t)row * D,
+                          scale, out + (size_t)row * D, lse ? lse + row : NULL,
                           wsum ? wsum + row : NULL);
     }
     return err;

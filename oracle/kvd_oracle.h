@@ -61,6 +61,13 @@ typedef struct {
     int32_t window;             /* sliding window in keys (0 = whole cache): the
                                    query at position p sees keys
                                    max(0, p - window + 1) .. p */
+    /* Context-parallel shard (both may be NULL): the cache holds only the
+     * keys at global positions key_pos0[b] .. key_pos0[b] + seq_lens[b] - 1
+     * (local key i is global key key_pos0[b] + i), and new token t of
+     * sequence b sits at global position q_pos[b] + t.  NULL means
+     * key_pos0 = 0 and q_pos = seq_lens - T (the whole cache). */
+    const int32_t *key_pos0;    /* [B] */
+    const int32_t *q_pos;       /* [B] */
 } oracle_cache;
 
 /* Return codes: 0 ok, nonzero = bad descriptor (nothing written). */
@@ -71,20 +78,22 @@ int oracle_rope(const double *x, double *y, int32_t n_rows, int32_t n_heads,
                 int32_t head_dim, const int64_t *positions, double base,
                 int32_t layout);
 
-/* RoPE the new q and k at position seq_lens[b] - T + t, store round(k_rot)
- * and round(v) into the cache slot that the block table names, and return
- * the rotated q in fp64.  q: [B][T][Hq][D]; k, v: [B][T][Hkv][D]; q_rot:
+/* RoPE the new q and k at their global position p = q_pos[b] + t (default
+ * seq_lens[b] - T + t), store round(k_rot) and round(v) into the slot of
+ * local key p - key_pos0[b] that the block table names, and return the
+ * rotated q in fp64.  q: [B][T][Hq][D]; k, v: [B][T][Hkv][D]; q_rot:
  * [B][T][Hq][D]. */
 int oracle_rope_append_kv(const oracle_cache *c, const float *q,
                           const float *k, const float *v, double *q_rot,
                           double base, int32_t layout);
 
 /* Attention of every query row against the cache as it stands.  Query t of
- * sequence b sees keys 0 .. seq_lens[b] - T + t (inclusive), or the last
- * `window` of them.  out:
- * [B][T][Hq][D]; lse (optional, may be NULL): [B][T][Hq] natural-log
+ * sequence b, at global position p, sees the keys at global positions
+ * 0 .. p (inclusive), or the last `window` of them, that the cache holds.
+ * out: [B][T][Hq][D]; lse (optional, may be NULL): [B][T][Hq] natural-log
  * log-sum-exp of the scaled scores; wsum (optional): [B][T][Hq] sum of the
- * normalised softmax weights (1 up to rounding). */
+ * normalised softmax weights (1 up to rounding).  A row that sees no key
+ * gets out = 0, lse = -inf and wsum = 0. */
 int oracle_decode_attention(const oracle_cache *c, const double *q_rot,
                             double scale, double *out, double *lse,
                             double *wsum);

@@ -468,6 +468,95 @@ def check_sliding_window_equals_truncated_cache():
         assert np.array_equal(out[:, t], one.decode_attention(np.ascontiguousarray(q[:, t:t + 1]))[:, 0])
 
 
+def _shard_cache(w, whole, cut0, cut1, window=0, q_tokens=None, dtype="f64"):
+    """A cache that holds only global keys cut0[b] .. cut1[b]-1 of each
+    sequence of `whole`, moved to local positions 0.., with the shard
+    positions that say so."""
+    s = w.spec
+    bs = s.block_size
+    n = (cut1 - cut0).astype(np.int64)
+    nb = max(1, int(max((k + bs - 1) // bs for k in n)))
+    fill = workloads.BF16_NAN if whole.k_pool.dtype == np.uint16 else np.nan
+    kp = np.full((s.num_seqs * nb, s.n_kv_heads, bs, s.head_dim), fill, whole.k_pool.dtype)
+    vp = np.full_like(kp, fill)
+    table = np.arange(s.num_seqs * nb, dtype=np.int32).reshape(s.num_seqs, nb)
+    for b in range(s.num_seqs):
+        for i, gpos in enumerate(range(int(cut0[b]), int(cut1[b]))):
+            blk = w.block_table[b, gpos // bs]
+            kp[table[b, i // bs], :, i % bs] = whole.k_pool[blk, :, gpos % bs]
+            vp[table[b, i // bs], :, i % bs] = whole.v_pool[blk, :, gpos % bs]
+    T = q_tokens or s.q_tokens
+    return oracle.OracleCache(num_seqs=s.num_seqs, q_tokens=T, n_q_heads=s.n_q_heads,
+                              n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, block_size=bs,
+                              k_pool=kp, v_pool=vp, block_table=table, seq_lens=n.astype(np.int32),
+                              cache_dtype=whole.cache_dtype, window=window,
+                              key_pos0=cut0.astype(np.int32),
+                              q_pos=(w.seq_lens - T).astype(np.int32))
+
+
+def check_context_parallel_shards_merge_to_whole():
+    """Context parallelism: each shard's (out, lse) over the keys it holds,
+    merged by log-sum-exp weights, equals attention over the whole cache;
+    a row that sees no key of a shard gets out = 0 and lse = -inf."""
+    from scipy.special import logsumexp
+    for window, seed in ((0, 21), (9, 22), (40, 23)):
+        w, oc = _tiny_cache(B=4, T=2, L=(0, 60), seed=seed)
+        s = w.spec
+        q = w.q.astype(np.float64) * 2.0
+        out_w, lse_w = oracle_cache(w, k_pool=oc.k_pool, v_pool=oc.v_pool, dtype="f64",
+                                    window=window).decode_attention(q, want_lse=True)
+        rng = np.random.default_rng(seed)
+        L = w.seq_lens.astype(np.int64)
+        # three shards per sequence at seeded cut points (empty shards included)
+        cuts = np.sort(np.stack([rng.integers(0, L + 1) for _ in range(2)], 1), 1)
+        cuts[0] = 0                      # sequence 0: two empty shards
+        cuts[1] = L[1] - 1               # sequence 1: the last shard holds only key L-1,
+                                         # which draft row 0 does not see
+        edges = np.concatenate([np.zeros((s.num_seqs, 1), np.int64), cuts, L[:, None]], 1)
+        outs, lses = [], []
+        for k in range(3):
+            sh = _shard_cache(w, oc, edges[:, k], edges[:, k + 1], window=window)
+            o, l_ = sh.decode_attention(q, want_lse=True)
+            empty = np.isneginf(l_)
+            assert np.all(o[empty] == 0.0)
+            outs.append(o)
+            lses.append(l_)
+        assert any(np.isneginf(l_).any() for l_ in lses), "want a shard some row cannot see"
+        lse_m = logsumexp(np.stack(lses), axis=0)
+        wts = np.exp(np.stack(lses) - lse_m)[..., None]
+        out_m = np.sum(wts * np.stack(outs), axis=0)
+        assert np.max(np.abs(out_m - out_w)) < 1e-12, window
+        assert np.max(np.abs(lse_m - lse_w)) < 1e-12, window
+
+
+def check_shard_append_rotates_at_global_position():
+    """The shard holding a sequence's tail appends its new tokens at their
+    global positions (the rotation) into its local slots: the stored rows and
+    q_rot equal the whole-cache append's bit for bit."""
+    for dtype, kvd in (("f64", "f64"), ("bf16", "bf16")):
+        spec = workloads.Spec("shard_append", 3, 2, 4, 2, 16, 4, kvd if kvd == "bf16" else "f32",
+                              (5, 50), 10000.0, "normal", "shuffled", spare_frac=0.2, seed=24)
+        w = workloads.make_workload(spec)
+        whole = oracle_cache(w, dtype=dtype)
+        q_whole = whole.rope_append_kv(w.q, w.k, w.v, spec.rope_base)
+        L = w.seq_lens.astype(np.int64)
+        cut = (L - spec.q_tokens) // 2
+        tail = _shard_cache(w, oracle_cache(w, dtype=dtype), cut, L, dtype=dtype)
+        q_tail = tail.rope_append_kv(w.q, w.k, w.v, spec.rope_base)
+        assert np.array_equal(q_whole, q_tail)
+        bs = spec.block_size
+        for b in range(spec.num_seqs):
+            for t in range(spec.q_tokens):
+                gpos = int(L[b]) - spec.q_tokens + t
+                loc = gpos - int(cut[b])
+                a = whole.k_pool[w.block_table[b, gpos // bs], :, gpos % bs]
+                c = tail.k_pool[tail.block_table[b, loc // bs], :, loc % bs]
+                assert np.array_equal(a, c), (dtype, b, t)
+                a = whole.v_pool[w.block_table[b, gpos // bs], :, gpos % bs]
+                c = tail.v_pool[tail.block_table[b, loc // bs], :, loc % bs]
+                assert np.array_equal(a, c), (dtype, b, t)
+
+
 def check_rows_api():
     w, oc = _tiny_cache(B=3, T=2, L=(3, 40), seed=13)
     q = w.q.astype(np.float64)

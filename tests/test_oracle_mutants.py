@@ -16,21 +16,26 @@ MUTANTS = {
     "rope_pairing": ("ia = 2 * i;", "ia = i;"),
     "q_position": ("rope_one(x, q_rot + o, D, pos, base, layout);",
                    "rope_one(x, q_rot + o, D, pos + 1, base, layout);"),
-    "gqa_mapping": ("err |= attend_row(c, b, h / g, n_vis, q_rot + (size_t)row * D, scale,\n"
-                    "                          out + (size_t)row * D,",
-                    "err |= attend_row(c, b, h % c->n_kv_heads, n_vis, q_rot + (size_t)row * D, scale,\n"
-                    "                          out + (size_t)row * D,"),
-    "visible_range": ("int64_t n_vis = (int64_t)c->seq_lens[b] - T + t + 1;\n        err |= attend_row(c, b, h / g, n_vis, q_rot + (size_t)row * D, scale,\n                          out + (size_t)row * D,",
-                      "int64_t n_vis = (int64_t)c->seq_lens[b] - T + t;\n        err |= attend_row(c, b, h / g, n_vis, q_rot + (size_t)row * D, scale,\n                          out + (size_t)row * D,"),
-    "no_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
-    "no_running_max": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "gqa_mapping": ("err |= attend_row(c, b, h / g, q_pos0(c, b) + t, q_rot + (size_t)row * D,\n"
+                    "                          scale, out + (size_t)row * D, lse ? lse + row : NULL,",
+                    "err |= attend_row(c, b, h % c->n_kv_heads, q_pos0(c, b) + t, q_rot + (size_t)row * D,\n"
+                    "                          scale, out + (size_t)row * D, lse ? lse + row : NULL,"),
+    "visible_range": ("err |= attend_row(c, b, h / g, q_pos0(c, b) + t, q_rot + (size_t)row * D,\n"
+                      "                          scale, out + (size_t)row * D, lse ? lse + row : NULL,",
+                      "err |= attend_row(c, b, h / g, q_pos0(c, b) + t - 1, q_rot + (size_t)row * D,\n"
+                      "                          scale, out + (size_t)row * D, lse ? lse + row : NULL,"),
+    "no_scale": ("s[j - i0] = scale * dot;", "s[j - i0] = dot;"),
+    "no_running_max": ("s[j - i0] = exp(s[j - i0] - m);", "s[j - i0] = exp(s[j - i0]);"),
     "slot_offset": ("int64_t off = pos % c->block_size;", "int64_t off = 0;"),
     "v_from_k_pool": ("out[d] += w * load(c, c->v_pool, idx + d);",
                       "out[d] += w * load(c, c->k_pool, idx + d);"),
     "ties_away": ("double n = nearbyint(a / quantum);", "double n = floor(a / quantum + 0.5);"),
     "double_rounding": ("double a = fabs(x);", "double a = fabs((double)(float)x);"),
     "k_not_rotated": ("store(c, c->k_pool, s + d, y[d]);", "store(c, c->k_pool, s + d, x[d]);"),
-    "window_off_by_one": ("? n_vis - c->window : 0;", "? n_vis - c->window + 1 : 0;"),
+    "window_off_by_one": ("? p + 1 - c->window : 0;", "? p + 2 - c->window : 0;"),
+    "shard_key_offset": ("int64_t i0 = g0 - k0, i1 = p + 1 - k0;", "int64_t i0 = g0, i1 = p + 1;"),
+    "shard_append_slot": ("int64_t local = pos - key_pos0(c, b);", "int64_t local = pos;"),
+    "shard_empty_lse": ("*lse = -INFINITY;", "*lse = 0.0;"),
 }
 
 
