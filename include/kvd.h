@@ -86,9 +86,26 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *                       block block_table[b][p / bs], slot p % bs.
  *   block_table         int32 [B][max_blocks_per_seq], physical block ids.
  *   seq_lens            int32 [B]: keys of each sequence INCLUDING its T new
- *                       tokens (seq_lens[b] >= T).  New token t of sequence b
+ *                       tokens (seq_lens[b] >= T unless q_pos is given).  New
+ *                       token t of sequence b
  *                       sits at position seq_lens[b] - T + t and its query
  *                       sees keys 0 .. seq_lens[b] - T + t.
+ *   key_pos0, q_pos     context-parallel shard (CP/DCP, one of the parallel
+ *                       modes of the ferrite page), both int32 [B] device
+ *                       arrays or NULL.  The cache then holds only the keys at
+ *                       global positions key_pos0[b] .. key_pos0[b] +
+ *                       seq_lens[b] - 1 (local key i = global key key_pos0[b]
+ *                       + i), and new token t sits at global position q_pos[b]
+ *                       + t: its query sees the held keys at global positions
+ *                       up to q_pos[b] + t (and inside the window).  NULL
+ *                       means key_pos0 = 0 and q_pos = key_pos0 +
+ *                       seq_lens - T, the whole cache; with q_pos given,
+ *                       seq_lens[b] may be below T (a shard without the new
+ *                       tokens).  kvd_rope_append_kv rotates at the global
+ *                       position and stores at local slot q_pos[b] + t -
+ *                       key_pos0[b], which must lie in [0, seq_lens[b]).  A
+ *                       row that sees no key of the shard gets out = 0 (and
+ *                       lse = -inf from kvd_decode_attention_lse).
  */
 typedef struct kvd_paged_kv {
     int32_t num_seqs;
@@ -106,6 +123,8 @@ typedef struct kvd_paged_kv {
     void *v_cache;
     const int32_t *block_table;
     const int32_t *seq_lens;
+    const int32_t *key_pos0;
+    const int32_t *q_pos;
 } kvd_paged_kv;
 
 /*
@@ -122,8 +141,9 @@ typedef struct kvd_paged_kv {
  * Angles and rotations are evaluated in fp64; q_rot is that value rounded to
  * fp32, the cache receives it rounded to kv_dtype (round-to-nearest-even, a
  * single rounding), and v is stored rounded to kv_dtype.  Exactly the B*T
- * target slots of each pool are written.  Only seq_lens, block_table and the
- * pools are read from the descriptor's device memory.
+ * target slots of each pool are written.  Only seq_lens, block_table, the
+ * shard positions (if any) and the pools are read from the descriptor's
+ * device memory.
  */
 int32_t kvd_rope_append_kv(const kvd_paged_kv *kv, const float *q, const float *k,
                            const float *v, float *q_rot, double rope_base,
@@ -178,6 +198,34 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv *kv, const float *q_rot, floa
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Decode attention that also exports each row's log-sum-exp, the partial a
+ * context-parallel shard hands to the merge (kvd_merge_partials).
+ *
+ *   lse    fp32 [B][T][Hq]: log(sum_j exp(scale * q.K_j)) in natural-log
+ *          units over the keys the row sees in this cache; -inf (and out = 0)
+ *          for a row that sees none.
+ * Everything else as kvd_decode_attention_ex (same workspace size).
+ */
+int32_t kvd_decode_attention_lse(const kvd_paged_kv *kv, const float *q_rot, float *out,
+                                 float *lse, float softmax_scale, const kvd_attn_options *opt,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Merge n_parts partial attention results of the same rows (one per
+ * context-parallel shard, gathered into one buffer):
+ *     LSE = log sum_p exp(lse_p),  out = sum_p exp(lse_p - LSE) * out_p.
+ *
+ *   n_parts   >= 1 (at most 4096).
+ *   rows      query rows per part (B*T*Hq); head_dim D as for the cache.
+ *   outs      fp32 [n_parts][rows][D];  lses  fp32 [n_parts][rows].
+ *   out       fp32 [rows][D];  lse_out fp32 [rows] or NULL.
+ * Parts with lse = -inf drop out; a row with every part at -inf gets out = 0
+ * and lse -inf.  out may not alias outs.
+ */
+int32_t kvd_merge_partials(int32_t n_parts, int64_t rows, int32_t head_dim, const float *outs,
+                           const float *lses, float *out, float *lse_out, void *stream);
+
+/*
  * The whole decode step in one call: kvd_rope_append_kv followed by
  * kvd_decode_attention_ex (generate.rs `step_gpu`: RoPE of the new q/k at the
  * token's position, the append, then `mha_decode_t` over the cache; the
@@ -191,7 +239,8 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv *kv, const float *q_rot, floa
  *           as for kvd_decode_attention_ex (same workspace size).
  *
  * Results (out, q_rot, the cache) are bitwise those of the two calls in a
- * row with the same plan.  When the plan uses the matrix-core kernel, one
+ * row with the same plan.  When the plan uses the matrix-core kernel and the
+ * descriptor is not a context-parallel shard, one
  * kernel does all of it (plus the split combine when there are several
  * splits): each workgroup rotates its own query rows, and the workgroup whose
  * key range holds the new tokens stores their K/V rows and uses them directly.
@@ -210,7 +259,8 @@ const char *kvd_status_string(int32_t status);
  * thread-local storage; "" if none). */
 const char *kvd_last_error(void);
 
-/* ABI version, bumped on any incompatible change (2: kvd_paged_kv.window). */
+/* ABI version, bumped on any incompatible change (2: kvd_paged_kv.window;
+ * 3: kvd_paged_kv.key_pos0 and .q_pos). */
 int32_t kvd_abi_version(void);
 
 #ifdef __cplusplus

@@ -25,8 +25,8 @@ KVD_KERNEL_AUTO, KVD_KERNEL_VALU, KVD_KERNEL_MFMA = 0, 1, 2
 EXPORTED = [
     "kvd_rope_append_kv", "kvd_decode_attention", "kvd_decode_attention_ex",
     "kvd_decode_attention_workspace_size", "kvd_decode_attention_workspace_size_ex",
-    "kvd_decode_attention_plan", "kvd_decode_step", "kvd_status_string", "kvd_last_error",
-    "kvd_abi_version",
+    "kvd_decode_attention_plan", "kvd_decode_step", "kvd_decode_attention_lse", "kvd_merge_partials",
+    "kvd_status_string", "kvd_last_error", "kvd_abi_version",
 ]
 
 
@@ -47,6 +47,8 @@ class KvdPagedKV(ctypes.Structure):
         ("v_cache", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p),
+        ("key_pos0", ctypes.c_void_p),
+        ("q_pos", ctypes.c_void_p),
     ]
 
 
@@ -90,6 +92,10 @@ def lib():
         L.kvd_decode_step.argtypes = [KV, P, P, P, P, P, ctypes.c_double, I32, ctypes.c_float, OPT,
                                       P, SZ, P]
         L.kvd_decode_step.restype = I32
+        L.kvd_decode_attention_lse.argtypes = [KV, P, P, P, ctypes.c_float, OPT, P, SZ, P]
+        L.kvd_decode_attention_lse.restype = I32
+        L.kvd_merge_partials.argtypes = [I32, ctypes.c_int64, I32, P, P, P, P, P]
+        L.kvd_merge_partials.restype = I32
         L.kvd_status_string.argtypes = [I32]
         L.kvd_status_string.restype = ctypes.c_char_p
         L.kvd_last_error.argtypes = []
@@ -140,6 +146,9 @@ class PagedKV:
     seq_lens:         int32 [B], keys per sequence including the T new tokens.
     max_seq_len:      host-side bound on seq_lens (sizes the split-K plan).
     window:           sliding window in keys (0 = the whole cache).
+    key_pos0, q_pos:  int32 [B] or None: a context-parallel shard holding the
+                      keys at global positions key_pos0 .. key_pos0 +
+                      seq_lens - 1, with new token t at global q_pos + t.
     """
     k_cache: torch.Tensor
     v_cache: torch.Tensor
@@ -149,6 +158,8 @@ class PagedKV:
     q_tokens_per_seq: int
     max_seq_len: int
     window: int = 0
+    key_pos0: Optional[torch.Tensor] = None
+    q_pos: Optional[torch.Tensor] = None
 
     def __post_init__(self):
         if self.k_cache.dtype not in (torch.bfloat16, torch.float32):
@@ -161,6 +172,10 @@ class PagedKV:
             raise ValueError("k/v_cache must be 4-D, block_table 2-D and seq_lens 1-D")
         if self.block_table.shape[0] != self.seq_lens.shape[0]:
             raise ValueError("block_table and seq_lens disagree on the batch size")
+        for name in ("key_pos0", "q_pos"):
+            t = getattr(self, name)
+            if t is not None:
+                _need(t, name, torch.int32, (self.num_seqs,))
 
     @property
     def num_seqs(self):
@@ -185,7 +200,9 @@ class PagedKV:
             int(self.block_table.shape[1]), int(self.max_seq_len),
             KVD_KV_BF16 if self.k_cache.dtype == torch.bfloat16 else KVD_KV_F32, int(self.window),
             self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.block_table.data_ptr(),
-            self.seq_lens.data_ptr())
+            self.seq_lens.data_ptr(),
+            self.key_pos0.data_ptr() if self.key_pos0 is not None else None,
+            self.q_pos.data_ptr() if self.q_pos is not None else None)
 
     def q_shape(self):
         return (self.num_seqs, self.q_tokens_per_seq, self.n_q_heads, self.head_dim)
@@ -300,3 +317,47 @@ def decode_step(kv: PagedKV, q, k, v, out=None, q_rot=None, want_q_rot=False, ro
                                  _opts(num_splits, kernel), wptr, wbytes, _stream_handle(stream)),
            "kvd_decode_step")
     return (out, q_rot) if q_rot is not None else out
+
+
+def decode_attention_lse(kv: PagedKV, q_rot, out=None, lse=None, softmax_scale=0.0, workspace_buf=None,
+                         num_splits=0, kernel=KVD_KERNEL_AUTO, stream=None):
+    """kvd_decode_attention_lse: decode attention plus each row's natural-log
+    log-sum-exp (a context-parallel shard's partial).  Returns (out, lse)."""
+    _need(q_rot, "q_rot", torch.float32, kv.q_shape())
+    if out is None:
+        out = torch.empty_like(q_rot)
+    if lse is None:
+        lse = torch.empty(kv.q_shape()[:3], dtype=torch.float32, device=q_rot.device)
+    _need(out, "out", torch.float32, kv.q_shape())
+    _need(lse, "lse", torch.float32, kv.q_shape()[:3])
+    if workspace_buf is None:
+        workspace_buf = workspace(kv, num_splits, kernel)
+    wptr = workspace_buf.data_ptr() if workspace_buf is not None else None
+    wbytes = workspace_buf.numel() * workspace_buf.element_size() if workspace_buf is not None else 0
+    d = kv.struct()
+    _check(lib().kvd_decode_attention_lse(ctypes.byref(d), q_rot.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr(), float(softmax_scale), _opts(num_splits, kernel),
+                                          wptr, wbytes, _stream_handle(stream)),
+           "kvd_decode_attention_lse")
+    return out, lse
+
+
+def merge_partials(outs, lses, out=None, lse_out=None, stream=None):
+    """kvd_merge_partials: outs fp32 [P][rows..][D], lses fp32 [P][rows..] ->
+    (out [rows..][D], lse [rows..])."""
+    if outs.dim() < 2 or lses.shape != outs.shape[:-1]:
+        raise ValueError("outs must be [P][...][D] and lses [P][...]")
+    _need(outs, "outs", torch.float32)
+    _need(lses, "lses", torch.float32)
+    P, D = int(outs.shape[0]), int(outs.shape[-1])
+    rows = int(lses[0].numel())
+    if out is None:
+        out = torch.empty(outs.shape[1:], dtype=torch.float32, device=outs.device)
+    if lse_out is None:
+        lse_out = torch.empty(lses.shape[1:], dtype=torch.float32, device=outs.device)
+    _need(out, "out", torch.float32, outs.shape[1:])
+    _need(lse_out, "lse_out", torch.float32, lses.shape[1:])
+    _check(lib().kvd_merge_partials(P, rows, D, outs.data_ptr(), lses.data_ptr(), out.data_ptr(),
+                                    lse_out.data_ptr(), _stream_handle(stream)),
+           "kvd_merge_partials")
+    return out, lse_out

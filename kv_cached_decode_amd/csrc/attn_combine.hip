@@ -67,7 +67,8 @@ __device__ inline bool combine_small(const AttnArgs& a, size_t qrow, int n) {
                 Ls += l[s] * w;
                 O += o[s] * w;
             }
-        a.out[qrow * c.D + d] = O / Ls;
+        a.out[qrow * c.D + d] = finish_out(O, Ls);
+        if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
     }
     return true;
 }
@@ -97,7 +98,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
         Ls = wave_sum(Ls);
         if (threadIdx.x == 0) {
             sm_red[0] = M;
-            sm_red[1] = 1.0f / Ls;
+            sm_red[1] = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+            if (a.lse) a.lse[qrow] = finish_lse(M, Ls);
         }
     }
     __syncthreads();
@@ -113,7 +115,56 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     }
 }
 
+// Merge of context-parallel partials: one workgroup per row.  Wave 0 forms
+// the parts' weights exp(lse_p - M) (M = max_p lse_p) in LDS and their sum S,
+// so LSE = M + log S; then each thread sums its elements over the parts with
+// a nonzero weight (a part that saw no key is never read) and scales by 1/S.
+// Fixed summation order.
+constexpr int MAX_PARTS = 4096;
+
+__global__ __launch_bounds__(COMBINE_THREADS) void merge_partials_kernel(int n, int64_t rows, int D,
+                                                                        const float* outs,
+                                                                        const float* lses, float* out,
+                                                                        float* lse_out) {
+    __shared__ float sm_w[MAX_PARTS];
+    __shared__ float sm_red[2];
+    const int64_t row = blockIdx.x;
+    if (threadIdx.x < 64) {
+        float M = -INFINITY;
+        for (int p = threadIdx.x; p < n; p += 64) M = fmaxf(M, lses[p * rows + row]);
+        M = wave_max(M);
+        float S = 0.0f;
+        for (int p = threadIdx.x; p < n; p += 64) {
+            const float w = M == -INFINITY ? 0.0f : expf(lses[p * rows + row] - M);
+            sm_w[p] = w;
+            S += w;
+        }
+        S = wave_sum(S);
+        if (threadIdx.x == 0) {
+            sm_red[0] = S > 0.0f ? M + logf(S) : -INFINITY;
+            sm_red[1] = S > 0.0f ? 1.0f / S : 0.0f;
+        }
+    }
+    __syncthreads();
+    if (lse_out && threadIdx.x == 0) lse_out[row] = sm_red[0];
+    const float inv = sm_red[1];
+    for (int d = threadIdx.x; d < D; d += COMBINE_THREADS) {
+        float o = 0.0f;
+        for (int p = 0; p < n; ++p)
+            if (sm_w[p] > 0.0f) o += sm_w[p] * outs[((size_t)p * rows + row) * D + d];
+        out[(size_t)row * D + d] = o * inv;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_merge_partials(int n_parts, int64_t rows, int D, const float* outs, const float* lses,
+                                 float* out, float* lse_out, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(merge_partials_kernel, dim3((unsigned)rows), dim3(COMBINE_THREADS), 0, s, n_parts,
+                       rows, D, outs, lses, out, lse_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
     const size_t rows = (size_t)a.c.B * a.c.T * a.c.Hq;

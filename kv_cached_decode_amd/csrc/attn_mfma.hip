@@ -152,22 +152,24 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // block it goes to, if the split holds new tokens
     float kx = 0.0f, ky = 0.0f, vx = 0.0f, vy = 0.0f;
     int kblk = 0;
-    auto split_begin = [&](int LL) { return range_start(c, LL) + split * a.split_keys; };
-    auto new_pair = [&](int bb, int LL, int idx, int& ia, int& ic, size_t& src) {
-        const int n0 = max(LL - c.T, split_begin(LL));
-        const int t = n0 + idx / HALF - (LL - c.T);
+    // qo: local index of the position of the sequence's first new token
+    auto split_begin = [&](int qo) { return range_start(c, qo) + split * a.split_keys; };
+    auto new_pair = [&](int bb, int qo, int idx, int& ia, int& ic, size_t& src) {
+        const int n0 = max(qo, split_begin(qo));
+        const int t = n0 + idx / HALF - qo;
         rope_pair(idx % HALF, HALF, a.interleaved, ia, ic);
         src = (((size_t)bb * c.T + t) * c.Hkv + kvh) * D;
     };
-    auto load_seq = [&](int bb, int LL) {
-        const int key_begin = split_begin(LL);
+    auto load_seq = [&](int bb, int LL, int qo) {
+        const int key_begin = split_begin(qo);
+        const int rend = range_end(c, LL, qo);
         if constexpr (FUSED) {
-            const int n0 = max(LL - c.T, key_begin);
-            const int n1 = min(LL, key_begin + a.split_keys);
+            const int n0 = max(qo, key_begin);
+            const int n1 = min(rend, key_begin + a.split_keys);
             if ((int)threadIdx.x < (n1 - n0) * HALF) {
                 int ia, ic;
                 size_t src;
-                new_pair(bb, LL, threadIdx.x, ia, ic, src);
+                new_pair(bb, qo, threadIdx.x, ia, ic, src);
                 const int i = threadIdx.x % HALF;
                 kx = a.k_new[src + ia];
                 ky = a.k_new[src + ic];
@@ -184,9 +186,9 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             xq[kk][0] = x0.x; xq[kk][1] = x0.y; xq[kk][2] = x0.z; xq[kk][3] = x0.w;
             xq[kk][4] = x1.x; xq[kk][5] = x1.y; xq[kk][6] = x1.z; xq[kk][7] = x1.w;
         }
-        if (key_begin < LL) {
+        if (key_begin < rend) {
             const int blk0 = key_begin >> c.log2_bs;
-            const int last = min(LL, key_begin + a.split_keys) - 1;
+            const int last = min(rend, key_begin + a.split_keys) - 1;
             const int nblk = min((last >> c.log2_bs) - blk0 + 1, MAX_PIECE_BLOCKS);
             if ((int)threadIdx.x < nblk) tb = c.table[(size_t)bb * c.max_blocks + blk0 + threadIdx.x];
         }
@@ -209,7 +211,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     }
     int b = z;
     int L = c.seq_lens[z];
-    load_seq(z, L);
+    int qo = q_local0(c, z, L);
+    load_seq(z, L, qo);
     if (c.B > 1 && c.B <= LPT_MAX_SEQS) {
         // the ranking borrows the V-tile LDS (unused until the key loop)
         int* sm_len = (int*)sm_v;
@@ -218,16 +221,18 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         b = lpt_rank_pick(c.B, z, sm_len, &sm_pick);
         if (b != z) {
             L = sm_len[b];
-            load_seq(b, L);
+            qo = q_local0(c, b, L);
+            load_seq(b, L, qo);
         }
     }
-    const int key_begin = split_begin(L);
-    if (key_begin >= L) {               // empty split
+    const int key_begin = split_begin(qo);
+    const int rend = range_end(c, L, qo);
+    if (key_begin >= rend) {            // empty split
         write_empty_partials(a, b, kvh, split, 0, a.rows);
         return;
     }
-    const int key_end = min(L, key_begin + a.split_keys);
-    const int vis = row_ok ? L - c.T + t_row : L - 1;     // last key this row sees
+    const int key_end = min(rend, key_begin + a.split_keys);
+    const int vis = qo + t_row;                            // last key this row sees
     const int lo = c.window > 0 ? vis - c.window + 1 : 0;  // first key it sees
 
     // Q^T operand for row n16: dims 32*kk + 8*j .. +8, scaled into log2 units
@@ -250,7 +255,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // LDS); the query rows rotated one pair per thread (rounded to fp32, as
     // q_rot); the new K/V rows that fall in this split rotated, rounded to
     // bf16, stored into the cache and kept in LDS for the tiles.
-    const int new0 = L - c.T;           // first new token's key index
+    const int new0 = qo;                // first new token's key index
     auto fused_angles = [&]() {
         static_assert(256 % HALF == 0, "a thread keeps its pair in every round");
         for (int idx = threadIdx.x; idx < c.T * HALF; idx += blockDim.x)
@@ -308,7 +313,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             const int key = n0 + idx / HALF, i = idx % HALF, t = key - new0;
             int ia, ic;
             size_t src;
-            new_pair(b, L, idx, ia, ic, src);
+            new_pair(b, qo, idx, ia, ic, src);
             if (idx >= (int)blockDim.x) {
                 kx = a.k_new[src + ia];
                 ky = a.k_new[src + ic];
@@ -519,7 +524,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         const int h = kvh * c.g + (r - t * c.g);
         const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h;
         if (a.num_splits == 1) {
-            a.out[qrow * D + d] = O / Ls;
+            a.out[qrow * D + d] = finish_out(O, Ls);
+            if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
         } else {
             a.part_o[(qrow * a.num_splits + split) * D + d] = O;
             if (d == 0) {

@@ -115,12 +115,14 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     const int b = blockIdx.z;
 
     const int L = c.seq_lens[b];
-    const int key_begin = range_start(c, L) + split * a.split_keys;
-    if (key_begin >= L) {                     // empty split
+    const int qo = q_local0(c, b, L);         // local index of the first new token's position
+    const int key_begin = range_start(c, qo) + split * a.split_keys;
+    const int rend = range_end(c, L, qo);
+    if (key_begin >= rend) {                  // empty split
         write_empty_partials(a, b, kvh, split, rtile * RT, RT);
         return;
     }
-    const int key_end = min(L, key_begin + a.split_keys);
+    const int key_end = min(rend, key_begin + a.split_keys);
 
     // stage the block ids of [key_begin, key_end) in LDS
     const int blk0 = key_begin >> c.log2_bs;
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         const bool ok = row < a.rows;
         const int t = ok ? row / c.g : 0;
         const int h = kvh * c.g + (ok ? row - t * c.g : 0);
-        vis[r] = ok ? L - c.T + t : -1;       // last visible key (inclusive)
+        vis[r] = ok ? qo + t : -1;            // last visible key (inclusive)
         lo[r] = c.window > 0 ? vis[r] - c.window + 1 : 0;   // first visible key
         const float4* qp = (const float4*)(a.q + (((size_t)b * c.T + t) * c.Hq + h) * D + chunk * EPL);
 #pragma unroll
@@ -294,7 +296,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         const int h = kvh * c.g + (row - t * c.g);
         const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h;
         if (a.num_splits == 1) {
-            a.out[qrow * D + d] = O / Ls;
+            a.out[qrow * D + d] = finish_out(O, Ls);
+            if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
         } else {
             a.part_o[(qrow * a.num_splits + split) * D + d] = O;
             if (d == 0) {

@@ -78,7 +78,8 @@ int32_t check_desc(const kvd_paged_kv* kv) {
     if (kv->num_blocks < 1 || kv->max_blocks_per_seq < 1)
         return fail(KVD_ERR_SHAPE, "num_blocks = %d, max_blocks_per_seq = %d", kv->num_blocks,
                     kv->max_blocks_per_seq);
-    if (kv->max_seq_len < kv->q_tokens_per_seq)
+    // a context-parallel shard may hold fewer keys than new tokens (or none)
+    if (kv->max_seq_len < (kv->q_pos ? 0 : kv->q_tokens_per_seq))
         return fail(KVD_ERR_SHAPE, "max_seq_len = %d < q_tokens_per_seq = %d", kv->max_seq_len,
                     kv->q_tokens_per_seq);
     if ((int64_t)kv->max_seq_len > (int64_t)kv->max_blocks_per_seq * kv->block_size)
@@ -91,8 +92,9 @@ int32_t check_desc(const kvd_paged_kv* kv) {
         return fail(KVD_ERR_NULL, "k_cache, v_cache, block_table and seq_lens must be non-NULL");
     if (((uintptr_t)kv->k_cache | (uintptr_t)kv->v_cache) & 15)
         return fail(KVD_ERR_SHAPE, "k_cache and v_cache must be 16-byte aligned");
-    if (((uintptr_t)kv->block_table | (uintptr_t)kv->seq_lens) & 3)
-        return fail(KVD_ERR_SHAPE, "block_table and seq_lens must be 4-byte aligned");
+    if (((uintptr_t)kv->block_table | (uintptr_t)kv->seq_lens | (uintptr_t)kv->key_pos0 |
+         (uintptr_t)kv->q_pos) & 3)
+        return fail(KVD_ERR_SHAPE, "block_table, seq_lens, key_pos0 and q_pos must be 4-byte aligned");
     return KVD_OK;
 }
 
@@ -111,6 +113,8 @@ kvd::CacheView view_of(const kvd_paged_kv* kv) {
     c.k = kv->k_cache;
     c.v = kv->v_cache;
     c.window = kv->window;
+    c.key_pos0 = kv->key_pos0;
+    c.q_pos = kv->q_pos;
     return c;
 }
 
@@ -154,9 +158,9 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     const int log2_bs = ilog2(kv->block_size);
     // keys a sequence's queries can see at most: the whole cache, or the
     // window plus the draft
-    const int64_t max_len = kv->window > 0
+    const int64_t max_len = std::max<int64_t>(1, kv->window > 0
         ? std::min<int64_t>(kv->max_seq_len, (int64_t)kv->window + kv->q_tokens_per_seq - 1)
-        : kv->max_seq_len;
+        : kv->max_seq_len);
     int step, n_rtiles;
     int64_t max_keys = INT32_MAX, target;
     if (kernel == KVD_KERNEL_MFMA) {
@@ -280,13 +284,13 @@ struct FuseIn {
 // Decode attention; with `fuse`, q_rot is the raw q and the matrix-core
 // kernel also rotates it and appends the new K/V rows.  The descriptor has
 // been checked and num_seqs > 0.
-int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float softmax_scale,
-                  const kvd_attn_options* opt, void* workspace, size_t workspace_bytes, void* stream,
-                  const FuseIn* fuse) {
+int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float* lse,
+                  float softmax_scale, const kvd_attn_options* opt, void* workspace,
+                  size_t workspace_bytes, void* stream, const FuseIn* fuse) {
     int32_t st;
     if (!q_rot || !out) return fail(KVD_ERR_NULL, "q and out must be non-NULL");
-    if (((uintptr_t)q_rot | (uintptr_t)out) & 3)
-        return fail(KVD_ERR_SHAPE, "q and out must be 4-byte aligned");
+    if (((uintptr_t)q_rot | (uintptr_t)out | (uintptr_t)lse) & 3)
+        return fail(KVD_ERR_SHAPE, "q, out and lse must be 4-byte aligned");
     if (!std::isfinite(softmax_scale))
         return fail(KVD_ERR_SHAPE, "softmax_scale must be finite");
     Plan p;
@@ -312,6 +316,7 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float 
     a.out = out;
     a.part_o = nullptr;
     a.part_ml = nullptr;
+    a.lse = lse;
     a.fused = fuse != nullptr;
     a.interleaved = fuse && fuse->layout == KVD_ROPE_INTERLEAVED;
     if (fuse) fill_theta(&a.theta, fuse->rope_base, kv->head_dim);
@@ -337,7 +342,7 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float 
 
 extern "C" {
 
-int32_t kvd_abi_version(void) { return 2; }
+int32_t kvd_abi_version(void) { return 3; }
 
 int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, const float* v,
                         float* q_rot, float* out, double rope_base, int32_t layout,
@@ -352,17 +357,17 @@ int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, 
     Plan p;
     st = make_plan(kv, opt, &p);
     if (st != KVD_OK) return st;
-    if (p.kernel == KVD_KERNEL_MFMA) {
+    if (p.kernel == KVD_KERNEL_MFMA && !kv->key_pos0 && !kv->q_pos) {
         const FuseIn f{k, v, q_rot, rope_base, layout};
-        return attention(kv, q, out, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
+        return attention(kv, q, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
     }
-    // vector-ALU plans: the two kernels in a row; `out` holds the rotated
-    // queries when the caller wants none back (each output row is written
-    // only after its query row has been read)
+    // vector-ALU plans and context-parallel shards: the two kernels in a
+    // row; `out` holds the rotated queries when the caller wants none back
+    // (each output row is written only after its query row has been read)
     float* qr = q_rot ? q_rot : out;
     st = rope_append(kv, q, k, v, qr, rope_base, layout, stream);
     if (st != KVD_OK) return st;
-    return attention(kv, qr, out, softmax_scale, opt, workspace, workspace_bytes, stream, nullptr);
+    return attention(kv, qr, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* kvd_status_string(int32_t s) {
@@ -427,7 +432,36 @@ int32_t kvd_decode_attention_ex(const kvd_paged_kv* kv, const float* q_rot, floa
     int32_t st = check_desc(kv);
     if (st != KVD_OK) return st;
     if (kv->num_seqs == 0) return ok();
-    return attention(kv, q_rot, out, softmax_scale, opt, workspace, workspace_bytes, stream, nullptr);
+    return attention(kv, q_rot, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+int32_t kvd_decode_attention_lse(const kvd_paged_kv* kv, const float* q_rot, float* out, float* lse,
+                                 float softmax_scale, const kvd_attn_options* opt, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (kv->num_seqs == 0) return ok();
+    if (!lse) return fail(KVD_ERR_NULL, "lse must be non-NULL");
+    return attention(kv, q_rot, out, lse, softmax_scale, opt, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+int32_t kvd_merge_partials(int32_t n_parts, int64_t rows, int32_t head_dim, const float* outs,
+                           const float* lses, float* out, float* lse_out, void* stream) {
+    if (n_parts < 1 || n_parts > 4096)
+        return fail(n_parts < 1 ? KVD_ERR_SHAPE : KVD_ERR_UNSUPPORTED, "n_parts = %d (supported 1..4096)",
+                    n_parts);
+    if (rows < 0 || head_dim < 1) return fail(KVD_ERR_SHAPE, "rows = %lld, head_dim = %d", (long long)rows, head_dim);
+    if (rows > 0x7fffffffLL) return fail(KVD_ERR_UNSUPPORTED, "rows = %lld (at most 2^31 - 1)", (long long)rows);
+    if (rows == 0) return ok();
+    if (!outs || !lses || !out) return fail(KVD_ERR_NULL, "outs, lses and out must be non-NULL");
+    if (((uintptr_t)outs | (uintptr_t)lses | (uintptr_t)out | (uintptr_t)lse_out) & 3)
+        return fail(KVD_ERR_SHAPE, "outs, lses, out and lse_out must be 4-byte aligned");
+    hipError_t e = kvd::launch_merge_partials(n_parts, rows, head_dim, outs, lses, out, lse_out,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "merge launch: %s", hipGetErrorString(e));
+    return ok();
 }
 
 int32_t kvd_decode_attention(const kvd_paged_kv* kv, const float* q_rot, float* out,

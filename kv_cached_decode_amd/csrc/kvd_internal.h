@@ -18,14 +18,27 @@ struct CacheView {
     void* k;                // [num_blocks][Hkv][bs][D]
     void* v;
     int32_t window;         // sliding window in keys, 0 = none
+    const int32_t* key_pos0;  // [B] context-parallel shard: global position of local key 0, or null
+    const int32_t* q_pos;     // [B] global position of new token 0, or null
 };
 
-// First key any query of a sequence with L keys can see: 0, or the start of
-// the first draft token's window.  Split s of a sequence covers
-// [range_start + s*split_keys, min(L, range_start + (s+1)*split_keys)).
-__device__ inline int range_start(const CacheView& c, int L) {
-    return c.window > 0 ? max(0, L - c.T - c.window + 1) : 0;
+// Local index of the position of a sequence's new token 0 (the last key its
+// first query sees): seq_lens - T for a whole cache; q_pos - key_pos0 for a
+// context-parallel shard, which may lie past the shard's keys (all of them
+// visible) or before them (none).
+__device__ inline int q_local0(const CacheView& c, int b, int L) {
+    if (!c.q_pos) return L - c.T;
+    return c.q_pos[b] - (c.key_pos0 ? c.key_pos0[b] : 0);
 }
+
+// Keys any query of a sequence can see: [range_start, range_end), from the
+// start of the first query's window (0 without one) to the last query's
+// position.  Split s covers [range_start + s*split_keys, min(range_end,
+// range_start + (s+1)*split_keys)).
+__device__ inline int range_start(const CacheView& c, int qo) {
+    return c.window > 0 ? max(0, qo - c.window + 1) : 0;
+}
+__device__ inline int range_end(const CacheView& c, int L, int qo) { return max(0, min(L, qo + c.T)); }
 
 // theta_i = rope_base^(-2i/D) for i < D/2, evaluated on the host.
 struct RopeTheta {
@@ -57,6 +70,7 @@ struct AttnArgs {
     float* out;             // [B][T][Hq][D] (written directly when S == 1)
     float* part_o;          // [B][T][Hq][S][D]   unnormalised partial outputs
     float* part_ml;         // [B][T][Hq][S][2]   (running max in log2 units, sum)
+    float* lse;             // [B][T][Hq] natural-log log-sum-exp of the row, or null
     // Fused decode step (matrix-core kernel only): q holds the raw queries;
     // the kernel rotates them, appends the new K/V rows of its split to the
     // cache and writes the rotated queries to q_rot when that is non-null.
@@ -70,10 +84,11 @@ struct AttnArgs {
 
 // A split that holds no key of its sequence leaves, for its rows, a partial
 // that drops out of the merge (running max -1e30, sum 0, output 0), so the
-// merge combines every split without reading the sequence lengths.
+// merge combines every split without reading the sequence lengths.  With a
+// single split (only a context-parallel shard can hold no key of a
+// sequence) the rows are final: output 0, lse -inf.
 __device__ inline void write_empty_partials(const AttnArgs& a, int b, int kvh, int split, int row0,
                                             int nrows) {
-    if (a.num_splits == 1) return;
     const CacheView& c = a.c;
     const int D = c.D;
     for (int idx = threadIdx.x; idx < nrows * (D + 2); idx += blockDim.x) {
@@ -81,6 +96,11 @@ __device__ inline void write_empty_partials(const AttnArgs& a, int b, int kvh, i
         if (r >= a.rows) continue;
         const int t = r / c.g;
         const size_t qrow = ((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g);
+        if (a.num_splits == 1) {
+            if (e < D) a.out[qrow * D + e] = 0.0f;
+            else if (e == D && a.lse) a.lse[qrow] = -INFINITY;
+            continue;
+        }
         const size_t part = qrow * a.num_splits + split;
         if (e < D) a.part_o[part * D + e] = 0.0f;
         else a.part_ml[part * 2 + (e - D)] = e == D ? -1e30f : 0.0f;
@@ -91,6 +111,16 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge_partials(int n_parts, int64_t rows, int D, const float* outs, const float* lses,
+                                 float* out, float* lse_out, hipStream_t s);
+
+// The finished row from its running max M (log2 units), sum Ls and
+// unnormalised output O: out = O / Ls, lse = (M + log2 Ls) ln 2; a row that
+// saw no key (Ls = 0) gets out = 0 and lse = -inf.
+__device__ inline float finish_out(float O, float Ls) { return Ls > 0.0f ? O / Ls : 0.0f; }
+__device__ inline float finish_lse(float M, float Ls) {
+    return Ls > 0.0f ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+}
 
 // Kernel-family properties the planner needs.
 int valu_step_keys(int D, int kv_bf16);      // keys per workgroup step

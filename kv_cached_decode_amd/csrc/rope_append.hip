@@ -4,7 +4,8 @@
 // per-item positions, paged KV through a block table).
 //
 // One workgroup per new token (b, t).  The token's position is
-// seq_lens[b] - T + t.  The D/2 rotation angles pos * theta_i (theta_i =
+// seq_lens[b] - T + t (in a context-parallel shard: q_pos[b] + t, stored at
+// local slot q_pos[b] + t - key_pos0[b]).  The D/2 rotation angles pos * theta_i (theta_i =
 // base^(-2i/D) from the host) are evaluated once per token in fp64 and shared
 // through LDS; every head's pair
 // is then rotated in fp64 and rounded once: to fp32 for q_rot and an fp32
@@ -54,8 +55,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
             x1 = a.v[o + 1];
         }
     }
-    const int pos = c.seq_lens[b] - c.T + t;
-    const int blk = c.table[(size_t)b * c.max_blocks + (pos >> c.log2_bs)];
+    // the token's local slot, and its global position for the rotation (they
+    // differ in a context-parallel shard)
+    const int local = q_local0(c, b, c.seq_lens[b]) + t;
+    const int pos = local + (c.key_pos0 ? c.key_pos0[b] : 0);
+    const int blk = c.table[(size_t)b * c.max_blocks + (local >> c.log2_bs)];
 
     for (int p = threadIdx.x; p < half; p += blockDim.x) rope_angle(a.theta.v[p], pos, cs[p], sn[p]);
     __syncthreads();
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
         return;
     }
     // the cache slot of this token
-    const int off = pos & ((1 << c.log2_bs) - 1);
+    const int off = local & ((1 << c.log2_bs) - 1);
     if (head < c.Hq + c.Hkv) {
         const int h = head - c.Hq;
         const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;

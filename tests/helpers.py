@@ -18,7 +18,7 @@ def pool_as_f64(w, pool):
 
 
 def oracle_cache(w, seq_lens=None, q_tokens=None, k_pool=None, v_pool=None, block_table=None,
-                 dtype=None, window=0):
+                 dtype=None, window=0, key_pos0=None, q_pos=None):
     """An OracleCache over copies of the workload's pools (or the given ones)."""
     s = w.spec
     dt = dtype or s.kv_dtype
@@ -32,7 +32,7 @@ def oracle_cache(w, seq_lens=None, q_tokens=None, k_pool=None, v_pool=None, bloc
         k_pool=np.ascontiguousarray(kp), v_pool=np.ascontiguousarray(vp),
         block_table=np.ascontiguousarray(w.block_table if block_table is None else block_table),
         seq_lens=np.ascontiguousarray(w.seq_lens if seq_lens is None else seq_lens, dtype=np.int32),
-        cache_dtype=ORACLE_DT[dt], window=window)
+        cache_dtype=ORACLE_DT[dt], window=window, key_pos0=key_pos0, q_pos=q_pos)
 
 
 def gather(pool_f64, table_row, bs, kvh, n):

@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     assert kb.status_name(0) == "KVD_OK"
     assert kb.status_name(4) == "KVD_ERR_WORKSPACE"
     assert kb.status_name(99) == "KVD_ERR_UNKNOWN"
-    assert kb.lib().kvd_abi_version() == 2
+    assert kb.lib().kvd_abi_version() == 3
 
 
 FAKE = 0x100000   # never dereferenced: every case below fails validation first
@@ -71,6 +71,8 @@ BAD = [
     (dict(block_table=0), kb.KVD_ERR_NULL),
     (dict(seq_lens=0), kb.KVD_ERR_NULL),
     (dict(k_cache=FAKE + 8), kb.KVD_ERR_SHAPE),           # misaligned
+    (dict(q_pos=FAKE + 0x40002), kb.KVD_ERR_SHAPE),       # misaligned shard positions
+    (dict(q_tokens_per_seq=4, max_seq_len=3, key_pos0=FAKE + 0x40000), kb.KVD_ERR_SHAPE),
 ]
 
 
@@ -86,6 +88,8 @@ def test_bad_descriptor_rejected_before_launch(kw, status):
     assert st == status, kb.last_error()
     st = L.kvd_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 10000.0, 0, 0.0, None, ws,
                            1 << 30, None)
+    assert st == status, kb.last_error()
+    st = L.kvd_decode_attention_lse(ctypes.byref(d), FAKE, FAKE, FAKE, 0.0, None, ws, 1 << 30, None)
     assert st == status, kb.last_error()
     assert L.kvd_decode_attention_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
 
@@ -198,3 +202,30 @@ def test_matrix_core_plan(B, T, Hq, Hkv):
             assert s <= forced
     _, _, kern = _plan(d, 0, 0)
     assert kern == (2 if (Hq // Hkv) * T >= 2 else 1)
+
+
+def test_lse_and_merge_arguments():
+    L = kb.lib()
+    d = desc(max_blocks_per_seq=64, max_seq_len=1000)
+    need = L.kvd_decode_attention_workspace_size(ctypes.byref(d))
+    assert L.kvd_decode_attention_lse(ctypes.byref(d), FAKE, FAKE, None, 0.0, None, FAKE, need,
+                                      None) == kb.KVD_ERR_NULL
+    assert L.kvd_decode_attention_lse(ctypes.byref(d), FAKE, FAKE, FAKE + 2, 0.0, None, FAKE, need,
+                                      None) == kb.KVD_ERR_SHAPE
+    M = L.kvd_merge_partials
+    assert M(0, 10, 128, FAKE, FAKE, FAKE, None, None) == kb.KVD_ERR_SHAPE
+    assert M(4097, 10, 128, FAKE, FAKE, FAKE, None, None) == kb.KVD_ERR_UNSUPPORTED
+    assert M(2, -1, 128, FAKE, FAKE, FAKE, None, None) == kb.KVD_ERR_SHAPE
+    assert M(2, 10, 0, FAKE, FAKE, FAKE, None, None) == kb.KVD_ERR_SHAPE
+    assert M(2, 10, 128, None, FAKE, FAKE, None, None) == kb.KVD_ERR_NULL
+    assert M(2, 10, 128, FAKE, FAKE, FAKE + 1, None, None) == kb.KVD_ERR_SHAPE
+    assert M(2, 0, 128, None, None, None, None, None) == kb.KVD_OK          # nothing to merge
+
+
+def test_shard_without_new_tokens_plans():
+    """A context-parallel shard may hold fewer keys than new tokens, even none
+    at all; it still gets a plan and a workspace size."""
+    d = desc(q_tokens_per_seq=4, max_seq_len=0, q_pos=FAKE + 0x40000, key_pos0=FAKE + 0x50000)
+    s, k, kern = _plan(d)
+    assert s >= 1 and k >= 1
+    assert kb.lib().kvd_decode_attention_workspace_size(ctypes.byref(d)) != ctypes.c_size_t(-1).value
