@@ -35,6 +35,7 @@ class _Cache(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("key_pos0", ctypes.c_void_p),
         ("q_pos", ctypes.c_void_p),
+        ("q_lens", ctypes.c_void_p),
     ]
 
 
@@ -94,7 +95,7 @@ class OracleCache:
 
     def __init__(self, *, num_seqs, q_tokens, n_q_heads, n_kv_heads, head_dim, block_size,
                  k_pool, v_pool, block_table, seq_lens, cache_dtype, window=0, key_pos0=None,
-                 q_pos=None):
+                 q_pos=None, q_lens=None):
         self.cache_dtype = cache_dtype
         dt = _DTYPES[cache_dtype]
         self.k_pool = _req(k_pool, dt)
@@ -107,12 +108,14 @@ class OracleCache:
         # context-parallel shard: global position of local key 0 and of new token 0
         self.key_pos0 = None if key_pos0 is None else _req(np.ascontiguousarray(key_pos0, np.int32), np.int32)
         self.q_pos = None if q_pos is None else _req(np.ascontiguousarray(q_pos, np.int32), np.int32)
+        # ragged new tokens per sequence (rows past q_lens[b] are padding)
+        self.q_lens = None if q_lens is None else _req(np.ascontiguousarray(q_lens, np.int32), np.int32)
         self._c = _Cache(self.num_seqs, self.q_tokens, self.n_q_heads, self.n_kv_heads,
                          self.head_dim, self.block_size, int(self.k_pool.shape[0]),
                          int(self.block_table.shape[1]) if self.block_table.ndim == 2 else 0,
                          cache_dtype, _ptr(self.k_pool), _ptr(self.v_pool),
                          _ptr(self.block_table), _ptr(self.seq_lens), int(window),
-                         _ptr(self.key_pos0), _ptr(self.q_pos))
+                         _ptr(self.key_pos0), _ptr(self.q_pos), _ptr(self.q_lens))
 
     def rope_append_kv(self, q, k, v, base, layout=ROPE_HALF):
         q = _req(q, np.float32)

@@ -128,6 +128,24 @@ int oracle_rope(const double *x, double *y, int32_t n_rows, int32_t n_heads,
     return 0;
 }
 
+/* New tokens of sequence b, the global position of local key 0, and that
+ * of new token 0 (by default the new tokens are the last keys held). */
+static int32_t n_new(const oracle_cache *c, int32_t b)
+{
+    return c->q_lens ? c->q_lens[b] : c->q_tokens;
+}
+
+static int64_t key_pos0(const oracle_cache *c, int32_t b)
+{
+    return c->key_pos0 ? (int64_t)c->key_pos0[b] : 0;
+}
+
+static int64_t q_pos0(const oracle_cache *c, int32_t b)
+{
+    return c->q_pos ? (int64_t)c->q_pos[b]
+                    : key_pos0(c, b) + (int64_t)c->seq_lens[b] - n_new(c, b);
+}
+
 static int check_cache(const oracle_cache *c)
 {
     if (!c || c->num_seqs < 0 || c->q_tokens < 1 || c->n_q_heads < 1 ||
@@ -140,7 +158,9 @@ static int check_cache(const oracle_cache *c)
         return 1;
     for (int32_t b = 0; b < c->num_seqs; ++b) {
         int64_t L = c->seq_lens[b];
-        if (L < (c->q_pos ? 0 : c->q_tokens))
+        if (c->q_lens && (c->q_lens[b] < 0 || c->q_lens[b] > c->q_tokens))
+            return 1;
+        if (L < (c->q_pos ? 0 : n_new(c, b)))
             return 1;
         int64_t nblk = (L + c->block_size - 1) / c->block_size;
         if (nblk > c->max_blocks_per_seq)
@@ -152,17 +172,6 @@ static int check_cache(const oracle_cache *c)
         }
     }
     return 0;
-}
-
-/* Global position of new token 0 of sequence b, and of local key 0. */
-static int64_t q_pos0(const oracle_cache *c, int32_t b)
-{
-    return c->q_pos ? (int64_t)c->q_pos[b] : (int64_t)c->seq_lens[b] - c->q_tokens;
-}
-
-static int64_t key_pos0(const oracle_cache *c, int32_t b)
-{
-    return c->key_pos0 ? (int64_t)c->key_pos0[b] : 0;
 }
 
 /* Flat element index of (local key pos of sequence b, kv head, dim 0). */
@@ -213,7 +222,7 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
         return 2;
     }
     for (int32_t b = 0; b < B; ++b)
-        for (int32_t t = 0; t < T; ++t) {
+        for (int32_t t = 0; t < n_new(c, b); ++t) {
             int64_t pos = q_pos0(c, b) + t;              /* global: the rotation */
             int64_t local = pos - key_pos0(c, b);        /* the cache slot */
             if (local < 0 || local >= c->seq_lens[b]) {
@@ -322,6 +331,13 @@ int oracle_decode_attention_rows(const oracle_cache *c, const double *q_rot,
         int32_t h = (int32_t)(row % Hq);
         int32_t t = (int32_t)((row / Hq) % T);
         int32_t b = (int32_t)(row / ((int64_t)Hq * T));
+        if (t >= n_new(c, b)) {            /* padding row */
+            for (int32_t d = 0; d < D; ++d)
+                out[(size_t)r * D + d] = 0.0;
+            if (lse)
+                lse[r] = -INFINITY;
+            continue;
+        }
         err |= attend_row(c, b, h / g, q_pos0(c, b) + t, q_rot + (size_t)row * D,
                           scale, out + (size_t)r * D, lse ? lse + r : NULL, NULL);
     }
@@ -343,6 +359,15 @@ int oracle_decode_attention(const oracle_cache *c, const double *q_rot,
         int32_t h = (int32_t)(row % Hq);
         int32_t t = (int32_t)((row / Hq) % T);
         int32_t b = (int32_t)(row / ((int64_t)Hq * T));
+        if (t >= n_new(c, b)) {            /* padding row */
+            for (int32_t d = 0; d < D; ++d)
+                out[(size_t)row * D + d] = 0.0;
+            if (lse)
+                lse[row] = -INFINITY;
+            if (wsum)
+                wsum[row] = 0.0;
+            continue;
+        }
         err |= attend_row(c, b, h / g, q_pos0(c, b) + t, q_rot + (size_t)row * D,
                           scale, out + (size_t)row * D, lse ? lse + row : NULL,
                           wsum ? wsum + row : NULL);

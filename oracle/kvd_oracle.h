@@ -68,6 +68,11 @@ typedef struct {
      * key_pos0 = 0 and q_pos = seq_lens - T (the whole cache). */
     const int32_t *key_pos0;    /* [B] */
     const int32_t *q_pos;       /* [B] */
+    /* Ragged new tokens (may be NULL = T for every sequence): sequence b has
+     * q_lens[b] <= T new tokens; rows t >= q_lens[b] are padding, appended
+     * nowhere and answered with out = 0, lse = -inf.  Without q_pos the new
+     * tokens are the last q_lens[b] keys of the cache. */
+    const int32_t *q_lens;      /* [B] */
 } oracle_cache;
 
 /* Return codes: 0 ok, nonzero = bad descriptor (nothing written). */

@@ -557,6 +557,55 @@ def check_shard_append_rotates_at_global_position():
                 assert np.array_equal(a, c), (dtype, b, t)
 
 
+def check_ragged_new_tokens():
+    """Ragged chunks (q_lens[b] <= T new tokens per sequence): each real row
+    equals the same sequence decoded alone with T = q_lens[b]; padding rows
+    get out = 0 and lse = -inf; the append writes exactly the real tokens'
+    slots (checked against a sentinel pool)."""
+    T = 6
+    spec = workloads.Spec("ragged", 4, T, 4, 2, 16, 4, "f32", (0, 30), 10000.0, "normal", "shuffled",
+                          spare_frac=0.2, seed=25)
+    w = workloads.make_workload(spec)
+    q_lens = np.array([6, 1, 3, 0], np.int32)
+    # the cache holds ctx + q_lens keys; the table covers ctx + T
+    sl = (w.ctx_lens + q_lens).astype(np.int32)
+    base = oracle_cache(w, seq_lens=sl, dtype="f64")
+    sentinel = np.full_like(base.k_pool, 7.0)
+    ragged = oracle.OracleCache(num_seqs=spec.num_seqs, q_tokens=T, n_q_heads=spec.n_q_heads,
+                                n_kv_heads=spec.n_kv_heads, head_dim=spec.head_dim,
+                                block_size=spec.block_size, k_pool=sentinel.copy(), v_pool=sentinel.copy(),
+                                block_table=w.block_table, seq_lens=sl, cache_dtype=oracle.ORACLE_F64,
+                                q_lens=q_lens)
+    q_rot = ragged.rope_append_kv(w.q, w.k, w.v, spec.rope_base)
+    changed = np.argwhere(np.any(ragged.k_pool != 7.0, axis=-1))
+    assert len(changed) == int(q_lens.sum()) * spec.n_kv_heads
+    bs = spec.block_size
+    for b in range(spec.num_seqs):
+        for t in range(int(q_lens[b])):
+            pos = int(sl[b]) - int(q_lens[b]) + t
+            assert np.all(ragged.k_pool[w.block_table[b, pos // bs], :, pos % bs] != 7.0)
+    # the same append into the real cache, then attention
+    full = oracle.OracleCache(num_seqs=spec.num_seqs, q_tokens=T, n_q_heads=spec.n_q_heads,
+                              n_kv_heads=spec.n_kv_heads, head_dim=spec.head_dim, block_size=bs,
+                              k_pool=base.k_pool, v_pool=base.v_pool, block_table=w.block_table,
+                              seq_lens=sl, cache_dtype=oracle.ORACLE_F64, q_lens=q_lens)
+    assert np.array_equal(full.rope_append_kv(w.q, w.k, w.v, spec.rope_base), q_rot)
+    out, lse = full.decode_attention(q_rot, want_lse=True)
+    assert np.all(np.isfinite(out))
+    for b in range(spec.num_seqs):
+        n = int(q_lens[b])
+        assert np.all(out[b, n:] == 0.0) and np.all(np.isneginf(lse[b, n:]))
+        if n == 0:
+            continue
+        one = oracle.OracleCache(num_seqs=1, q_tokens=n, n_q_heads=spec.n_q_heads,
+                                 n_kv_heads=spec.n_kv_heads, head_dim=spec.head_dim, block_size=bs,
+                                 k_pool=full.k_pool, v_pool=full.v_pool,
+                                 block_table=np.ascontiguousarray(w.block_table[b:b + 1]),
+                                 seq_lens=sl[b:b + 1], cache_dtype=oracle.ORACLE_F64)
+        o1, l1 = one.decode_attention(np.ascontiguousarray(q_rot[b:b + 1, :n]), want_lse=True)
+        assert np.array_equal(out[b, :n], o1[0]) and np.array_equal(lse[b, :n], l1[0])
+
+
 def check_rows_api():
     w, oc = _tiny_cache(B=3, T=2, L=(3, 40), seed=13)
     q = w.q.astype(np.float64)

@@ -36,6 +36,10 @@ MUTANTS = {
     "shard_key_offset": ("int64_t i0 = g0 - k0, i1 = p + 1 - k0;", "int64_t i0 = g0, i1 = p + 1;"),
     "shard_append_slot": ("int64_t local = pos - key_pos0(c, b);", "int64_t local = pos;"),
     "shard_empty_lse": ("*lse = -INFINITY;", "*lse = 0.0;"),
+    "ragged_positions": (": key_pos0(c, b) + (int64_t)c->seq_lens[b] - n_new(c, b);",
+                         ": key_pos0(c, b) + (int64_t)c->seq_lens[b] - c->q_tokens;"),
+    "ragged_padding_attended": ("if (t >= n_new(c, b)) {            /* padding row */\n            for (int32_t d = 0; d < D; ++d)\n                out[(size_t)row * D + d] = 0.0;",
+                                "if (t >= n_new(c, b) && 0) {       /* padding row */\n            for (int32_t d = 0; d < D; ++d)\n                out[(size_t)row * D + d] = 0.0;"),
 }
 
 
