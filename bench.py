@@ -36,9 +36,10 @@ from kv_cached_decode_amd import binding as kb  # noqa: E402
 from kv_cached_decode_amd import workloads  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 HEADLINE = "llama3_8b"
-KERNEL_SOURCES = ["kvd.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_combine.hip", "rope_append.hip",
-                  "kvd_internal.h", "bf16_round.h", "rope_math.h"]
+KERNEL_SOURCES = ["kvd.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_prefill.hip", "attn_combine.hip",
+                  "rope_append.hip", "kvd_internal.h", "bf16_round.h", "rope_math.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -65,12 +66,14 @@ class Layers:
         self.kernel, self.num_splits = kernel, num_splits
         table = torch.from_numpy(w.block_table).to(dev)
         seq_lens = torch.from_numpy(w.seq_lens).to(dev)
+        q_lens = torch.from_numpy(w.q_lens).to(dev) if w.q_lens is not None else None
         kd, vd = to_dev_pool(w.k_pool, dev), to_dev_pool(w.v_pool, dev)
         self.kv = []
         for i in range(n):
             k = kd if i == 0 else kd.clone()
             v = vd if i == 0 else vd.clone()
-            self.kv.append(kb.PagedKV(k, v, table, seq_lens, s.n_q_heads, s.q_tokens, w.max_seq_len))
+            self.kv.append(kb.PagedKV(k, v, table, seq_lens, s.n_q_heads, s.q_tokens, w.max_seq_len,
+                                      q_lens=q_lens))
         self.q = torch.from_numpy(w.q).to(dev)
         self.k = torch.from_numpy(w.k).to(dev)
         self.v = torch.from_numpy(w.v).to(dev)
@@ -126,7 +129,7 @@ def measure(name, steps, warmup, dev, kernel=0, num_splits=0):
     two_ms = timed(L.two_calls, steps, warmup)
     attn_ms = timed(L.attention, steps, warmup)
     nb = w.algorithmic_bytes()
-    tokens = s.num_seqs * s.q_tokens
+    tokens = int(w.q_lens.sum()) if w.q_lens is not None else s.num_seqs * s.q_tokens
     res = {
         "workload": name, "layers_rotated": n_layers, "plan": {"splits": L.plan[0], "keys_per_split": L.plan[1],
                                                                "kernel": ["auto", "valu", "mfma"][L.plan[2]]},
@@ -139,9 +142,60 @@ def measure(name, steps, warmup, dev, kernel=0, num_splits=0):
     }
     res["attn_frac_of_peak"] = res["attn_GBs"] / PEAK_HBM_GBS
     res["step_frac_of_peak"] = res["step_GBs"] / PEAK_HBM_GBS
+    if w.q_lens is not None:
+        # a prefill chunk leans on the matrix cores: algorithmic flops of the
+        # attention call against the dense bf16 peak
+        res["attn_TFLOPs"] = w.algorithmic_flops() / (attn_ms * 1e-3) / 1e12
+        res["attn_frac_of_bf16_peak"] = res["attn_TFLOPs"] / PEAK_BF16_TFLOPS
     del L
     torch.cuda.empty_cache()
     return w, res
+
+
+def measure_cp_shard(steps, warmup, dev, parts=8):
+    """One GPU's share of the long-context layer under context parallelism
+    over `parts` GPUs: a shard holding 131072/parts keys of each sequence
+    exports (out, lse) for every query row, then the `parts` partials are
+    merged.  The shards are the first parts-1 key ranges of the cache (each a
+    distinct 268 MB region, rotated like layers); the new token lies past
+    all of them, so every held key is visible."""
+    w = workloads.make_workload(workloads.CONFIGS["long_ctx"])
+    s = w.spec
+    ctx = int(w.seq_lens.min()) - s.q_tokens
+    n = ctx // parts
+    bs = s.block_size
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+    kd, vd = to_dev_pool(w.k_pool, dev), to_dev_pool(w.v_pool, dev)
+    kvs = []
+    for k in range(parts - 1):
+        table = w.block_table[:, (k * n) // bs:]
+        table = np.concatenate([table, np.full((s.num_seqs, (k * n) // bs), -1, np.int32)], 1)
+        kvs.append(kb.PagedKV(kd, vd, t(table), t(np.full(s.num_seqs, n)), s.n_q_heads, s.q_tokens, n,
+                              key_pos0=t(np.full(s.num_seqs, k * n)),
+                              q_pos=t(w.seq_lens.astype(np.int64) - s.q_tokens)))
+    q = torch.from_numpy(w.q).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = kb.workspace(kvs[0])
+    ws = ws.clone() if ws is not None else None
+    plan = kb.decode_attention_plan(kvs[0])
+    shard_ms = timed(lambda i: kb.decode_attention_lse(kvs[i % len(kvs)], q, out, lse, 0.0, ws), steps, warmup)
+    outs = torch.randn((parts,) + tuple(q.shape), dtype=torch.float32, device=dev)
+    lses = torch.randn((parts,) + tuple(q.shape[:3]), dtype=torch.float32, device=dev)
+    mo, ml = torch.empty_like(q), torch.empty_like(lse)
+    merge_ms = timed(lambda i: kb.merge_partials(outs, lses, mo, ml), steps, warmup)
+    rows = s.num_seqs * s.q_tokens * s.n_q_heads
+    shard_bytes = s.num_seqs * n * s.n_kv_heads * s.head_dim * 2 * 2 + rows * s.head_dim * 4 * 2 + rows * 4 \
+        + s.num_seqs * (n // bs) * 4
+    del kvs, kd, vd
+    torch.cuda.empty_cache()
+    return {"workload": f"long_ctx shard of {parts}: B={s.num_seqs} Hq={s.n_q_heads} Hkv={s.n_kv_heads} "
+                        f"D={s.head_dim}, {n} keys per sequence, exports (out, lse)",
+            "plan": {"splits": plan[0], "keys_per_split": plan[1], "kernel": ["auto", "valu", "mfma"][plan[2]]},
+            "shard_ms": round(shard_ms, 4), "shard_GBs": round(shard_bytes / (shard_ms * 1e-3) / 1e9, 1),
+            "shard_frac_of_peak": round(shard_bytes / (shard_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "merge_ms": round(merge_ms, 4),
+            "exchange_bytes_per_gpu": rows * (s.head_dim + 1) * 4}
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -359,6 +413,7 @@ def main():
             steps = max(10, args.steps // 4)
             _, r = measure(name, steps, max(2, args.warmup // 4), dev, args.kernel, args.splits)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        extra["long_ctx_cp8_shard"] = measure_cp_shard(max(10, args.steps // 4), max(2, args.warmup // 4), dev)
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     s = w.spec

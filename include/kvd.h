@@ -64,7 +64,9 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *
  *   num_seqs            B, sequences in the batch (>= 0; 0 is a no-op).
  *   q_tokens_per_seq    T, new tokens per sequence: 1 = decode, >1 = verify of
- *                       a T-token draft, causal within the draft.  1..16.
+ *                       a T-token draft or a prefill chunk, causal within it.
+ *                       1..1024 (more than 16 query rows per kv head run
+ *                       through the prefill kernel).
  *   n_q_heads           Hq; n_kv_heads Hkv; Hq % Hkv == 0.  Query head h
  *                       reads kv head h / (Hq / Hkv).
  *   head_dim            D in {16, 32, 64, 128, 256}.
@@ -106,6 +108,14 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *                       key_pos0[b], which must lie in [0, seq_lens[b]).  A
  *                       row that sees no key of the shard gets out = 0 (and
  *                       lse = -inf from kvd_decode_attention_lse).
+ *   q_lens              int32 [B] device array or NULL (= T for every
+ *                       sequence): ragged chunks, sequence b brings q_lens[b]
+ *                       <= T new tokens (chunked prefill with a different
+ *                       chunk per sequence, drafts of different lengths).
+ *                       They are the last q_lens[b] keys (or sit at q_pos[b]
+ *                       + t); rows t >= q_lens[b] are padding: not appended,
+ *                       their q_rot rows left as they are and their out rows
+ *                       0 (lse -inf).  seq_lens[b] >= q_lens[b].
  */
 typedef struct kvd_paged_kv {
     int32_t num_seqs;
@@ -125,6 +135,7 @@ typedef struct kvd_paged_kv {
     const int32_t *seq_lens;
     const int32_t *key_pos0;
     const int32_t *q_pos;
+    const int32_t *q_lens;
 } kvd_paged_kv;
 
 /*
@@ -260,7 +271,7 @@ const char *kvd_status_string(int32_t status);
 const char *kvd_last_error(void);
 
 /* ABI version, bumped on any incompatible change (2: kvd_paged_kv.window;
- * 3: kvd_paged_kv.key_pos0 and .q_pos). */
+ * 3: kvd_paged_kv.key_pos0, .q_pos and .q_lens). */
 int32_t kvd_abi_version(void);
 
 #ifdef __cplusplus

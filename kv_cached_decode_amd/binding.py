@@ -49,6 +49,7 @@ class KvdPagedKV(ctypes.Structure):
         ("seq_lens", ctypes.c_void_p),
         ("key_pos0", ctypes.c_void_p),
         ("q_pos", ctypes.c_void_p),
+        ("q_lens", ctypes.c_void_p),
     ]
 
 
@@ -149,6 +150,8 @@ class PagedKV:
     key_pos0, q_pos:  int32 [B] or None: a context-parallel shard holding the
                       keys at global positions key_pos0 .. key_pos0 +
                       seq_lens - 1, with new token t at global q_pos + t.
+    q_lens:           int32 [B] or None: ragged chunks, q_lens[b] <= T new
+                      tokens per sequence (rows past them are padding).
     """
     k_cache: torch.Tensor
     v_cache: torch.Tensor
@@ -160,6 +163,7 @@ class PagedKV:
     window: int = 0
     key_pos0: Optional[torch.Tensor] = None
     q_pos: Optional[torch.Tensor] = None
+    q_lens: Optional[torch.Tensor] = None
 
     def __post_init__(self):
         if self.k_cache.dtype not in (torch.bfloat16, torch.float32):
@@ -172,7 +176,7 @@ class PagedKV:
             raise ValueError("k/v_cache must be 4-D, block_table 2-D and seq_lens 1-D")
         if self.block_table.shape[0] != self.seq_lens.shape[0]:
             raise ValueError("block_table and seq_lens disagree on the batch size")
-        for name in ("key_pos0", "q_pos"):
+        for name in ("key_pos0", "q_pos", "q_lens"):
             t = getattr(self, name)
             if t is not None:
                 _need(t, name, torch.int32, (self.num_seqs,))
@@ -202,7 +206,8 @@ class PagedKV:
             self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.block_table.data_ptr(),
             self.seq_lens.data_ptr(),
             self.key_pos0.data_ptr() if self.key_pos0 is not None else None,
-            self.q_pos.data_ptr() if self.q_pos is not None else None)
+            self.q_pos.data_ptr() if self.q_pos is not None else None,
+            self.q_lens.data_ptr() if self.q_lens is not None else None)
 
     def q_shape(self):
         return (self.num_seqs, self.q_tokens_per_seq, self.n_q_heads, self.head_dim)

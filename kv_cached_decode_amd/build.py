@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kvd.cpp", "rope_append.hip", "attn_valu.hip", "attn_mfma.hip", "attn_combine.hip"]
+SOURCES = ["kvd.cpp", "rope_append.hip", "attn_valu.hip", "attn_mfma.hip", "attn_prefill.hip",
+           "attn_combine.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

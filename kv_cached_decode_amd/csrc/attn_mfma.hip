@@ -162,7 +162,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     };
     auto load_seq = [&](int bb, int LL, int qo) {
         const int key_begin = split_begin(qo);
-        const int rend = range_end(c, LL, qo);
+        const int rend = range_end(c, LL, qo, n_new(c, bb));
         if constexpr (FUSED) {
             const int n0 = max(qo, key_begin);
             const int n1 = min(rend, key_begin + a.split_keys);
@@ -225,14 +225,16 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             load_seq(b, L, qo);
         }
     }
+    const int nn = n_new(c, b);          // new tokens of this sequence (rows past them: padding)
     const int key_begin = split_begin(qo);
-    const int rend = range_end(c, L, qo);
+    const int rend = range_end(c, L, qo, nn);
     if (key_begin >= rend) {            // empty split
         write_empty_partials(a, b, kvh, split, 0, a.rows);
         return;
     }
     const int key_end = min(rend, key_begin + a.split_keys);
-    const int vis = qo + t_row;                            // last key this row sees
+    const bool row_live = row_ok && t_row < nn;
+    const int vis = row_live ? qo + t_row : -1;            // last key this row sees
     const int lo = c.window > 0 ? vis - c.window + 1 : 0;  // first key it sees
 
     // Q^T operand for row n16: dims 32*kk + 8*j .. +8, scaled into log2 units
@@ -284,7 +286,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             const float x1 = (float)xr, y1 = (float)yr;
             sm_q[r * D + ia] = x1;
             sm_q[r * D + ic] = y1;
-            if (a.q_rot && split == 0) {
+            if (a.q_rot && split == 0 && t < nn) {
                 float* qr = a.q_rot + (((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g)) * D;
                 qr[ia] = x1;
                 qr[ic] = y1;

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     const int L = c.seq_lens[b];
     const int qo = q_local0(c, b, L);         // local index of the first new token's position
     const int key_begin = range_start(c, qo) + split * a.split_keys;
-    const int rend = range_end(c, L, qo);
+    const int nn = n_new(c, b);               // new tokens (rows past them: padding)
+    const int rend = range_end(c, L, qo, nn);
     if (key_begin >= rend) {                  // empty split
         write_empty_partials(a, b, kvh, split, rtile * RT, RT);
         return;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int row = row0 + r;
-        const bool ok = row < a.rows;
+        const bool ok = row < a.rows && row / c.g < nn;
         const int t = ok ? row / c.g : 0;
         const int h = kvh * c.g + (ok ? row - t * c.g : 0);
         vis[r] = ok ? qo + t : -1;            // last visible key (inclusive)

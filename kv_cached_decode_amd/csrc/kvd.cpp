@@ -60,9 +60,9 @@ int32_t check_desc(const kvd_paged_kv* kv) {
     if (!kv) return fail(KVD_ERR_NULL, "descriptor is NULL");
     if (kv->num_seqs < 0) return fail(KVD_ERR_SHAPE, "num_seqs = %d < 0", kv->num_seqs);
     if (kv->num_seqs == 0) return KVD_OK;
-    if (kv->q_tokens_per_seq < 1 || kv->q_tokens_per_seq > 16)
+    if (kv->q_tokens_per_seq < 1 || kv->q_tokens_per_seq > 1024)
         return fail(kv->q_tokens_per_seq < 1 ? KVD_ERR_SHAPE : KVD_ERR_UNSUPPORTED,
-                    "q_tokens_per_seq = %d (supported 1..16)", kv->q_tokens_per_seq);
+                    "q_tokens_per_seq = %d (supported 1..1024)", kv->q_tokens_per_seq);
     if (kv->n_q_heads < 1 || kv->n_kv_heads < 1)
         return fail(KVD_ERR_SHAPE, "head counts must be >= 1 (Hq=%d, Hkv=%d)", kv->n_q_heads,
                     kv->n_kv_heads);
@@ -78,8 +78,9 @@ int32_t check_desc(const kvd_paged_kv* kv) {
     if (kv->num_blocks < 1 || kv->max_blocks_per_seq < 1)
         return fail(KVD_ERR_SHAPE, "num_blocks = %d, max_blocks_per_seq = %d", kv->num_blocks,
                     kv->max_blocks_per_seq);
-    // a context-parallel shard may hold fewer keys than new tokens (or none)
-    if (kv->max_seq_len < (kv->q_pos ? 0 : kv->q_tokens_per_seq))
+    // a context-parallel shard may hold fewer keys than new tokens (or none),
+    // and ragged chunks fewer new tokens than T
+    if (kv->max_seq_len < (kv->q_pos || kv->q_lens ? 0 : kv->q_tokens_per_seq))
         return fail(KVD_ERR_SHAPE, "max_seq_len = %d < q_tokens_per_seq = %d", kv->max_seq_len,
                     kv->q_tokens_per_seq);
     if ((int64_t)kv->max_seq_len > (int64_t)kv->max_blocks_per_seq * kv->block_size)
@@ -93,8 +94,8 @@ int32_t check_desc(const kvd_paged_kv* kv) {
     if (((uintptr_t)kv->k_cache | (uintptr_t)kv->v_cache) & 15)
         return fail(KVD_ERR_SHAPE, "k_cache and v_cache must be 16-byte aligned");
     if (((uintptr_t)kv->block_table | (uintptr_t)kv->seq_lens | (uintptr_t)kv->key_pos0 |
-         (uintptr_t)kv->q_pos) & 3)
-        return fail(KVD_ERR_SHAPE, "block_table, seq_lens, key_pos0 and q_pos must be 4-byte aligned");
+         (uintptr_t)kv->q_pos | (uintptr_t)kv->q_lens) & 3)
+        return fail(KVD_ERR_SHAPE, "block_table, seq_lens, key_pos0, q_pos and q_lens must be 4-byte aligned");
     return KVD_OK;
 }
 
@@ -115,11 +116,13 @@ kvd::CacheView view_of(const kvd_paged_kv* kv) {
     c.window = kv->window;
     c.key_pos0 = kv->key_pos0;
     c.q_pos = kv->q_pos;
+    c.q_lens = kv->q_lens;
     return c;
 }
 
 struct Plan {
     int kernel;       // KVD_KERNEL_VALU / KVD_KERNEL_MFMA
+    bool prefill;     // matrix cores with more than 16 query rows per kv head
     int splits;
     int split_keys;
     int rows;
@@ -147,13 +150,15 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     int kernel = opt ? opt->kernel : KVD_KERNEL_AUTO;
     if (kernel != KVD_KERNEL_AUTO && kernel != KVD_KERNEL_VALU && kernel != KVD_KERNEL_MFMA)
         return fail(KVD_ERR_UNSUPPORTED, "kernel = %d", kernel);
-    const bool mfma_ok = kvd::mfma_supported(D, bf16, p->rows);
+    // the matrix-core kernels: the decode kernel up to 16 query rows per kv
+    // head, the prefill kernel (64-row tiles sharing LDS-staged K/V) beyond
+    const bool mfma_ok = kvd::mfma_supported(D, bf16, 1);
     if (kernel == KVD_KERNEL_MFMA && !mfma_ok)
-        return fail(KVD_ERR_UNSUPPORTED,
-                    "MFMA kernel needs a bf16 cache, head_dim 128 and g*T <= 16 (rows = %d)", p->rows);
+        return fail(KVD_ERR_UNSUPPORTED, "matrix-core kernels need a bf16 cache and head_dim 128");
     if (kernel == KVD_KERNEL_AUTO)
         kernel = (mfma_ok && p->rows >= kvd::MFMA_MIN_ROWS) ? KVD_KERNEL_MFMA : KVD_KERNEL_VALU;
     p->kernel = kernel;
+    p->prefill = kernel == KVD_KERNEL_MFMA && !kvd::mfma_supported(D, bf16, p->rows);
 
     const int log2_bs = ilog2(kv->block_size);
     // keys a sequence's queries can see at most: the whole cache, or the
@@ -163,7 +168,15 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
         : kv->max_seq_len);
     int step, n_rtiles;
     int64_t max_keys = INT32_MAX, target;
-    if (kernel == KVD_KERNEL_MFMA) {
+    if (p->prefill) {
+        // compute-leaning: about two resident workgroups per CU, each split
+        // staging at most 4094 block ids
+        step = kvd::prefill_step_keys();
+        p->row_tile = kvd::PREFILL_ROWS;
+        n_rtiles = (int)cdiv(p->rows, kvd::PREFILL_ROWS);
+        max_keys = (int64_t)4094 << log2_bs;
+        target = 2 * (int64_t)num_cus();
+    } else if (kernel == KVD_KERNEL_MFMA) {
         step = kvd::mfma_step_keys();
         p->row_tile = 16;
         n_rtiles = 1;
@@ -196,6 +209,9 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     int64_t keys = cdiv(max_len, splits);
     splits = cdiv(max_len, keys);
     if (splits > 65535) return fail(KVD_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)splits);
+    if ((int64_t)kv->n_kv_heads * n_rtiles > 65535 || kv->num_seqs > 65535)
+        return fail(KVD_ERR_UNSUPPORTED, "grid too large: %d kv heads x %d row tiles, %d sequences",
+                    kv->n_kv_heads, n_rtiles, kv->num_seqs);
     p->splits = (int)splits;
     p->split_keys = (int)keys;
     return KVD_OK;
@@ -329,7 +345,9 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
         a.part_ml = (float*)((char*)workspace + cv.ml);
     }
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s) : kvd::launch_attn_valu(a, s);
+    hipError_t e = p.prefill                     ? kvd::launch_attn_prefill(a, s)
+                   : p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s)
+                                                 : kvd::launch_attn_valu(a, s);
     if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "decode attention launch: %s", hipGetErrorString(e));
     if (p.splits > 1) {
         e = kvd::launch_attn_combine(a, s);
@@ -357,12 +375,12 @@ int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, 
     Plan p;
     st = make_plan(kv, opt, &p);
     if (st != KVD_OK) return st;
-    if (p.kernel == KVD_KERNEL_MFMA && !kv->key_pos0 && !kv->q_pos) {
+    if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && !kv->key_pos0 && !kv->q_pos) {
         const FuseIn f{k, v, q_rot, rope_base, layout};
         return attention(kv, q, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
     }
-    // vector-ALU plans and context-parallel shards: the two kernels in a
-    // row; `out` holds the rotated queries when the caller wants none back
+    // vector-ALU and prefill plans and context-parallel shards: the two
+    // kernels in a row; `out` holds the rotated queries when the caller wants none back
     // (each output row is written only after its query row has been read)
     float* qr = q_rot ? q_rot : out;
     st = rope_append(kv, q, k, v, qr, rope_base, layout, stream);

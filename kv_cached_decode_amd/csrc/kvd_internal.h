@@ -20,14 +20,18 @@ struct CacheView {
     int32_t window;         // sliding window in keys, 0 = none
     const int32_t* key_pos0;  // [B] context-parallel shard: global position of local key 0, or null
     const int32_t* q_pos;     // [B] global position of new token 0, or null
+    const int32_t* q_lens;    // [B] new tokens per sequence (<= T), or null = T
 };
 
+// New tokens of sequence b (rows t >= n_new are padding).
+__device__ inline int n_new(const CacheView& c, int b) { return c.q_lens ? c.q_lens[b] : c.T; }
+
 // Local index of the position of a sequence's new token 0 (the last key its
-// first query sees): seq_lens - T for a whole cache; q_pos - key_pos0 for a
+// first query sees): seq_lens - n_new for a whole cache; q_pos - key_pos0 for a
 // context-parallel shard, which may lie past the shard's keys (all of them
 // visible) or before them (none).
 __device__ inline int q_local0(const CacheView& c, int b, int L) {
-    if (!c.q_pos) return L - c.T;
+    if (!c.q_pos) return L - n_new(c, b);
     return c.q_pos[b] - (c.key_pos0 ? c.key_pos0[b] : 0);
 }
 
@@ -38,7 +42,7 @@ __device__ inline int q_local0(const CacheView& c, int b, int L) {
 __device__ inline int range_start(const CacheView& c, int qo) {
     return c.window > 0 ? max(0, qo - c.window + 1) : 0;
 }
-__device__ inline int range_end(const CacheView& c, int L, int qo) { return max(0, min(L, qo + c.T)); }
+__device__ inline int range_end(const CacheView& c, int L, int qo, int nn) { return max(0, min(L, qo + nn)); }
 
 // theta_i = rope_base^(-2i/D) for i < D/2, evaluated on the host.
 struct RopeTheta {
@@ -111,6 +115,7 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_partials(int n_parts, int64_t rows, int D, const float* outs, const float* lses,
                                  float* out, float* lse_out, hipStream_t s);
 
@@ -129,6 +134,9 @@ int valu_max_row_tile(int D, int kv_bf16);   // rows one workgroup can hold
 constexpr int VALU_MAX_STAGED_BLOCKS = 4096;
 int valu_max_split_keys(int log2_bs);
 bool mfma_supported(int D, int kv_bf16, int rows);
+// Query rows of one prefill workgroup (more rows than the decode kernel takes).
+constexpr int PREFILL_ROWS = 64;
+int prefill_step_keys();
 int mfma_step_keys();
 // Resident workgroups per CU for a kernel variant (occupancy query on the
 // current device; a conservative default when there is none).

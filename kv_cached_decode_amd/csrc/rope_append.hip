@@ -29,6 +29,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const CacheView& c = a.c;
     const int token = blockIdx.x;
     const int b = token / c.T, t = token - b * c.T;
+    if (t >= n_new(c, b)) return;      // a padding token of a ragged chunk: nothing to rotate or store
     const int D = c.D, half = D >> 1;
     const int heads_per_wg = blockDim.x / half;
     const int head = blockIdx.y * heads_per_wg + (int)threadIdx.x / half;

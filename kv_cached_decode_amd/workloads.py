@@ -18,6 +18,9 @@ Workload shapes follow the five named configurations of the decode step:
   (block 64), values N(0,1) plus 16 seeded large-magnitude keys per sequence.
 * ``mtp_verify``     -- batch 32, 4 query tokens per sequence (causal within
   the draft), 32 q / 8 kv heads, context 16384, paged bf16 (block 16).
+* ``chunked_prefill`` -- batch 8 of Llama-3-8B-shaped layers taking a prefill
+  chunk each: ragged chunks of 64..512 new tokens (uniform per sequence) on
+  ragged contexts uniform in [0, 4096], paged bf16 (block 16, shuffled).
 
 bf16 values are drawn as float32 and truncated to their top 16 bits (a
 distribution choice, not a rounding the method performs).  Cache slots past
@@ -60,6 +63,7 @@ class Spec:
     prefix: bool = False               # cache built by appends from raw prefix tokens
     seed: int = 0
     layout: int = 0                    # RoPE pairing: 0 half, 1 interleaved
+    chunk: Optional[Tuple[int, int]] = None   # ragged new tokens per sequence, uniform [lo, hi] <= T
 
     def with_(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -76,8 +80,10 @@ CONFIGS = {
                      "shuffled", spare_frac=0.05, big_keys=16, seed=4),
     "mtp_verify": Spec("mtp_verify", 32, 4, 32, 8, 128, 16, "bf16", 16384, 10000.0, "normal",
                        "shuffled", spare_frac=0.05, seed=5),
+    "chunked_prefill": Spec("chunked_prefill", 8, 512, 32, 8, 128, 16, "bf16", (0, 4096), 500000.0,
+                            "normal_scaled", "shuffled", spare_frac=0.05, seed=7, chunk=(64, 512)),
 }
-CONFIG_ORDER = ["tiny_f32", "llama3_8b", "qwen3_0_6b_cb", "long_ctx", "mtp_verify"]
+CONFIG_ORDER = ["tiny_f32", "llama3_8b", "qwen3_0_6b_cb", "long_ctx", "mtp_verify", "chunked_prefill"]
 
 
 def small_variant(name: str) -> Spec:
@@ -94,6 +100,9 @@ def small_variant(name: str) -> Spec:
         return s.with_(name=name + "_small", num_seqs=2, ctx=9000, seed=104)
     if name == "mtp_verify":
         return s.with_(name=name + "_small", num_seqs=5, ctx=(0, 600), seed=105)
+    if name == "chunked_prefill":
+        return s.with_(name=name + "_small", num_seqs=3, q_tokens=96, ctx=(0, 300), chunk=(1, 96),
+                       seed=107)
     raise KeyError(name)
 
 
@@ -101,7 +110,7 @@ def small_variant(name: str) -> Spec:
 class Workload:
     spec: Spec
     ctx_lens: np.ndarray          # int64 [B], context before the step
-    seq_lens: np.ndarray          # int32 [B], keys after the T new tokens are appended
+    seq_lens: np.ndarray          # int32 [B], keys after the new tokens are appended
     block_table: np.ndarray       # int32 [B][max_blocks_per_seq], -1 = unused
     k_pool: np.ndarray            # [num_blocks][Hkv][bs][D] uint16 (bf16 bits) or float32
     v_pool: np.ndarray
@@ -112,6 +121,7 @@ class Workload:
     prefix_q: Optional[np.ndarray] = None      # float32 [B][P][Hq][D] raw prefix tokens
     prefix_k: Optional[np.ndarray] = None
     prefix_v: Optional[np.ndarray] = None
+    q_lens: Optional[np.ndarray] = None        # int32 [B] new tokens per sequence (ragged chunks)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -133,14 +143,29 @@ class Workload:
         esz = 2 if s.kv_dtype == "bf16" else 4
         keys = int(self.seq_lens.astype(np.int64).sum())
         kv_read = keys * Hkv * D * 2 * esz
-        qo = B * T * Hq * D * 4 * 2
+        if self.q_lens is not None:
+            T = float(np.mean(self.q_lens))        # real rows only
+        qo = int(B * T * Hq * D * 4 * 2)
         table = int(sum((int(L) + s.block_size - 1) // s.block_size for L in self.seq_lens)) * 4
         attn = kv_read + qo + table + B * 4
         rope_append = B * T * (Hq * D * 4 * 2 + 2 * Hkv * D * (4 + esz)) + B * 4 + B * T * 4
         # the whole step: the cache read, q in, out, the new k/v in and their
         # append, the block table and seq_lens (no intermediate q_rot)
-        step = attn + B * T * 2 * Hkv * D * (4 + esz)
-        return {"kv_read": kv_read, "attention": attn, "rope_append": rope_append, "step": step}
+        step = attn + int(B * T * 2 * Hkv * D * (4 + esz))
+        return {"kv_read": kv_read, "attention": attn, "rope_append": int(rope_append), "step": step}
+
+    def algorithmic_flops(self) -> int:
+        """Multiply-adds of the attention, 2 flops each: for every real query
+        row, q.K over the keys it sees and the weighted sum of their V rows."""
+        s = self.spec
+        T = s.q_tokens
+        n = self.q_lens if self.q_lens is not None else np.full(s.num_seqs, T)
+        total = 0
+        for b in range(s.num_seqs):
+            L, nb = int(self.seq_lens[b]), int(n[b])
+            vis = L - nb + 1 + np.arange(nb)                 # keys row t sees
+            total += int(vis.sum())
+        return total * s.n_q_heads * s.head_dim * 2 * 2
 
 
 def _draw(rng, n, dist, dtype_out):
@@ -187,7 +212,12 @@ def make_workload(spec: Spec) -> Workload:
         ctx = rng.integers(lo, hi + 1, size=B).astype(np.int64)
     else:
         ctx = np.full(B, int(spec.ctx), np.int64)
-    seq_lens = (ctx + T).astype(np.int32)
+    q_lens = None
+    if spec.chunk is not None:
+        lo, hi = spec.chunk
+        assert 0 <= lo <= hi <= T
+        q_lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+    seq_lens = (ctx + (T if q_lens is None else q_lens)).astype(np.int32)
     nblk = [(int(L) + bs - 1) // bs for L in seq_lens]
     max_blocks = max(nblk) if B else 0
     total = int(sum(nblk))
@@ -257,7 +287,7 @@ def make_workload(spec: Spec) -> Workload:
         q, k, v = raw((B, T, Hq, D)), raw((B, T, Hkv, D)), raw((B, T, Hkv, D))
     return Workload(spec, ctx, seq_lens, table, k_pool, v_pool,
                     np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v),
-                    big, pq, pk, pv)
+                    big, pq, pk, pv, q_lens)
 
 
 def sample_rows(spec: Spec, n: int, seed: int = 0) -> np.ndarray:

@@ -35,28 +35,42 @@ def cached_workload(spec):
     return workloads.make_workload(spec)
 
 
+def check_table(table, seq_lens, block_size, num_blocks):
+    """Host check before any launch: every block a sequence's keys need is
+    allocated (an id in the pool), so no kernel can address outside it."""
+    table = np.asarray(table)
+    for b, L in enumerate(np.asarray(seq_lens)):
+        need = table[b, :-(-int(L) // block_size)]
+        assert need.size == -(-int(L) // block_size), f"sequence {b}: table too narrow for {L} keys"
+        assert np.all((need >= 0) & (need < num_blocks)), f"sequence {b}: unallocated block for {L} keys"
+
+
 class GpuCase:
     """A workload resident on the GPU, ready for the step."""
 
-    def __init__(self, w, seq_lens=None, q_tokens=None, window=0, block_table=None):
+    def __init__(self, w, seq_lens=None, q_tokens=None, window=0, block_table=None, q_lens=None):
         self.w = w
         s = w.spec
         self.k_cache = to_dev_pool(w.k_pool)
         self.v_cache = to_dev_pool(w.v_pool)
         self.table = torch.from_numpy(w.block_table if block_table is None else block_table).to(DEV)
         sl = w.seq_lens if seq_lens is None else seq_lens
+        check_table(w.block_table if block_table is None else block_table, sl, s.block_size, w.num_blocks)
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(sl, dtype=np.int32)).to(DEV)
         T = q_tokens or s.q_tokens
+        ql = w.q_lens if q_lens is None else q_lens
+        self.q_lens = None if ql is None else torch.from_numpy(np.ascontiguousarray(ql, np.int32)).to(DEV)
         self.kv = kb.PagedKV(self.k_cache, self.v_cache, self.table, self.seq_lens, s.n_q_heads, T,
-                             max(int(np.max(sl)), T) if len(sl) else T, window)
+                             max(int(np.max(sl)), T) if len(sl) else T, window, q_lens=self.q_lens)
         self.q = torch.from_numpy(w.q).to(DEV)
         self.k = torch.from_numpy(w.k).to(DEV)
         self.v = torch.from_numpy(w.v).to(DEV)
 
     def step(self, kernel=kb.KVD_KERNEL_AUTO, num_splits=0, scale=0.0):
         s = self.w.spec
-        q_rot = kb.rope_append_kv(self.kv, self.q, self.k, self.v, rope_base=s.rope_base,
-                                  layout=s.layout)
+        # zeroed: the rows of padding tokens (ragged chunks) are left as they are
+        q_rot = kb.rope_append_kv(self.kv, self.q, self.k, self.v, torch.zeros_like(self.q),
+                                  rope_base=s.rope_base, layout=s.layout)
         out = kb.decode_attention(self.kv, q_rot, softmax_scale=scale, num_splits=num_splits,
                                   kernel=kernel)
         torch.cuda.synchronize()

@@ -17,9 +17,15 @@ def pool_as_f64(w, pool):
     return pool.astype(np.float64)
 
 
+_WORKLOAD_Q_LENS = object()
+
+
 def oracle_cache(w, seq_lens=None, q_tokens=None, k_pool=None, v_pool=None, block_table=None,
-                 dtype=None, window=0, key_pos0=None, q_pos=None):
-    """An OracleCache over copies of the workload's pools (or the given ones)."""
+                 dtype=None, window=0, key_pos0=None, q_pos=None, q_lens=_WORKLOAD_Q_LENS):
+    """An OracleCache over copies of the workload's pools (or the given ones);
+    ragged chunk lengths default to the workload's."""
+    if q_lens is _WORKLOAD_Q_LENS:
+        q_lens = w.q_lens
     s = w.spec
     dt = dtype or s.kv_dtype
     kp = np.array(w.k_pool if k_pool is None else k_pool, copy=True)
@@ -32,7 +38,7 @@ def oracle_cache(w, seq_lens=None, q_tokens=None, k_pool=None, v_pool=None, bloc
         k_pool=np.ascontiguousarray(kp), v_pool=np.ascontiguousarray(vp),
         block_table=np.ascontiguousarray(w.block_table if block_table is None else block_table),
         seq_lens=np.ascontiguousarray(w.seq_lens if seq_lens is None else seq_lens, dtype=np.int32),
-        cache_dtype=ORACLE_DT[dt], window=window, key_pos0=key_pos0, q_pos=q_pos)
+        cache_dtype=ORACLE_DT[dt], window=window, key_pos0=key_pos0, q_pos=q_pos, q_lens=q_lens)
 
 
 def gather(pool_f64, table_row, bs, kvh, n):

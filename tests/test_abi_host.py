@@ -53,7 +53,7 @@ def desc(**kw):
 BAD = [
     (dict(num_seqs=-1), kb.KVD_ERR_SHAPE),
     (dict(q_tokens_per_seq=0), kb.KVD_ERR_SHAPE),
-    (dict(q_tokens_per_seq=17), kb.KVD_ERR_UNSUPPORTED),
+    (dict(q_tokens_per_seq=1025), kb.KVD_ERR_UNSUPPORTED),
     (dict(n_q_heads=6, n_kv_heads=4), kb.KVD_ERR_SHAPE),
     (dict(n_kv_heads=0), kb.KVD_ERR_SHAPE),
     (dict(head_dim=96), kb.KVD_ERR_UNSUPPORTED),
@@ -64,6 +64,7 @@ BAD = [
     (dict(num_blocks=0), kb.KVD_ERR_SHAPE),
     (dict(max_seq_len=0), kb.KVD_ERR_SHAPE),
     (dict(q_tokens_per_seq=4, max_seq_len=3), kb.KVD_ERR_SHAPE),
+    (dict(q_lens=FAKE + 0x60001), kb.KVD_ERR_SHAPE),         # misaligned chunk lengths
     (dict(max_seq_len=129), kb.KVD_ERR_SHAPE),            # > 8 blocks * 16
     (dict(kv_dtype=2), kb.KVD_ERR_UNSUPPORTED),
     (dict(window=-1), kb.KVD_ERR_SHAPE),
@@ -229,3 +230,16 @@ def test_shard_without_new_tokens_plans():
     s, k, kern = _plan(d)
     assert s >= 1 and k >= 1
     assert kb.lib().kvd_decode_attention_workspace_size(ctypes.byref(d)) != ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("T", [5, 17, 64, 512, 1024])
+def test_prefill_plan(T):
+    """More than 16 query rows per kv head on the matrix cores: the prefill
+    kernel, whose splits cover every key; ragged chunks may leave the
+    length bound below T."""
+    d = desc(num_seqs=8, q_tokens_per_seq=T, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=400,
+             max_seq_len=max(T, 4096 + T))
+    s, k, kern = _plan(d)
+    assert kern == 2 and s * k >= 4096 + T and (s - 1) * k < 4096 + T
+    d = desc(num_seqs=2, q_tokens_per_seq=T, max_seq_len=1, q_lens=FAKE + 0x60000)
+    assert _plan(d)[0] >= 1

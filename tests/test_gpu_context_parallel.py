@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import DEV, GpuCase, assert_parity, cached_workload, note
+from gpu_common import DEV, GpuCase, assert_parity, cached_workload, check_table, note
 from helpers import oracle_cache
 from kv_cached_decode_amd import binding as kb
 from kv_cached_decode_amd import workloads
@@ -57,6 +57,7 @@ def shard_kv(case, cuts, k, window=0):
         row = w.block_table[b, first:]
         table[b, :row.size] = row
     n = (cuts[:, k + 1] - cuts[:, k]).astype(np.int32)
+    check_table(table, n, bs, w.num_blocks)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)  # noqa: E731
     return kb.PagedKV(case.k_cache, case.v_cache, t(table), t(n), s.n_q_heads, s.q_tokens,
                       max(1, int(n.max())), window, key_pos0=t(cuts[:, k]),

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 def two_calls(case, kernel=kb.KVD_KERNEL_AUTO, num_splits=0):
     s = case.w.spec
-    q_rot = kb.rope_append_kv(case.kv, case.q, case.k, case.v, rope_base=s.rope_base, layout=s.layout)
+    q_rot = kb.rope_append_kv(case.kv, case.q, case.k, case.v, torch.zeros_like(case.q),
+                              rope_base=s.rope_base, layout=s.layout)
     out = kb.decode_attention(case.kv, q_rot, kernel=kernel, num_splits=num_splits)
     torch.cuda.synchronize()
     return q_rot.cpu().numpy(), out.cpu().numpy()
@@ -27,7 +28,8 @@ def two_calls(case, kernel=kb.KVD_KERNEL_AUTO, num_splits=0):
 
 def fused(case, kernel=kb.KVD_KERNEL_AUTO, num_splits=0, want_q_rot=True):
     s = case.w.spec
-    res = kb.decode_step(case.kv, case.q, case.k, case.v, want_q_rot=want_q_rot,
+    res = kb.decode_step(case.kv, case.q, case.k, case.v,
+                         q_rot=torch.zeros_like(case.q) if want_q_rot else None,
                          rope_base=s.rope_base, layout=s.layout, kernel=kernel,
                          num_splits=num_splits)
     torch.cuda.synchronize()

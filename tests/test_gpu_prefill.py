@@ -1,0 +1,102 @@
+"""GPU: chunked prefill and other many-row cases (more than 16 query rows
+per kv head run through the prefill kernel) against the oracle, every row;
+ragged chunks (q_lens), the append of exactly the real tokens, windows,
+split counts, and agreement with the vector-ALU kernel."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import GpuCase, assert_parity, assert_qrot, note, oracle_step
+from kv_cached_decode_amd import binding as kb
+from kv_cached_decode_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(name, B, T, Hq, Hkv, ctx, seed, chunk=None, bs=16):
+    return workloads.Spec(name, B, T, Hq, Hkv, 128, bs, "bf16", ctx, 10000.0, "normal", "shuffled",
+                          spare_frac=0.1, seed=seed, chunk=chunk)
+
+
+CASES = [
+    spec("chunk64_g4", 2, 64, 32, 8, (100, 500), 61),          # uniform chunk, 256 rows per kv head
+    spec("chunk40_g8", 2, 40, 64, 8, (0, 300), 62),            # 320 rows, tile tails
+    spec("chunk33_mha", 2, 33, 8, 8, (50, 200), 63),           # g = 1: 33 rows
+    spec("ragged_g4", 4, 100, 32, 8, (0, 400), 64, chunk=(0, 100)),
+    spec("ragged_bs64", 3, 130, 16, 8, (200, 900), 65, chunk=(17, 130), bs=64),
+]
+
+
+@pytest.mark.parametrize("sp", CASES, ids=lambda s: s.name)
+def test_prefill_all_rows(sp):
+    w = workloads.make_workload(sp)
+    note("prefill", sp.name, "q_lens", None if w.q_lens is None else w.q_lens.tolist())
+    case = GpuCase(w)
+    assert kb.decode_attention_plan(case.kv)[2] == kb.KVD_KERNEL_MFMA
+    q_gpu, out = case.step()
+    kp, vp = case.pools()
+    q_ref, ref, kp_ref, vp_ref = oracle_step(w)
+    assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref), "append differs"
+    assert_qrot(q_gpu, q_ref)
+    if w.q_lens is not None:
+        for b, n in enumerate(w.q_lens):
+            assert np.all(out[b, n:] == 0.0), "padding rows must be 0"
+    assert_parity(sp, out, ref)
+
+
+def test_ragged_extremes():
+    """Chunks of 0, 1 and T tokens side by side (the workload allocates every
+    sequence a full chunk of T; the chunks below only lower the lengths)."""
+    sp = spec("ragged_extremes", 3, 48, 32, 8, (0, 200), 66, chunk=(48, 48))
+    w = workloads.make_workload(sp)
+    q_lens = np.array([0, 1, 48], np.int32)
+    sl = (w.ctx_lens + q_lens).astype(np.int32)
+    assert np.all(sl <= w.seq_lens)
+    note("ragged extremes")
+    case = GpuCase(w, seq_lens=sl, q_lens=q_lens)
+    q_gpu, out = case.step()
+    kp, vp = case.pools()
+    w2 = workloads.Workload(**{**w.__dict__, "seq_lens": sl, "q_lens": q_lens})
+    q_ref, ref, kp_ref, vp_ref = oracle_step(w2)
+    assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref)
+    assert np.all(out[0] == 0.0) and np.all(out[1, 1:] == 0.0)
+    assert_parity(sp, out, ref)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 9])
+def test_prefill_split_counts(splits):
+    sp = spec("prefill_splits", 2, 64, 32, 8, (300, 700), 67)
+    w = workloads.make_workload(sp)
+    note("prefill splits", splits)
+    case = GpuCase(w)
+    _, out = case.step(num_splits=splits)
+    _, ref, _, _ = oracle_step(w)
+    assert_parity(sp, out, ref)
+
+
+@pytest.mark.parametrize("window", [1, 20, 100])
+def test_prefill_window(window):
+    sp = spec("prefill_window", 2, 64, 32, 8, (100, 300), 68)
+    w = workloads.make_workload(sp)
+    note("prefill window", window)
+    case = GpuCase(w, window=window)
+    _, out = case.step()
+    _, ref, _, _ = oracle_step(w, window=window)
+    assert_parity(sp, out, ref)
+
+
+def test_prefill_and_valu_kernels_agree():
+    sp = spec("prefill_vs_valu", 2, 24, 32, 8, (0, 250), 69, chunk=(5, 24))
+    w = workloads.make_workload(sp)
+    note("prefill vs valu")
+    outs = {}
+    for kern in (kb.KVD_KERNEL_MFMA, kb.KVD_KERNEL_VALU):
+        case = GpuCase(w)
+        outs[kern] = case.step(kernel=kern)[1]
+        del case
+        torch.cuda.empty_cache()
+    _, ref, _, _ = oracle_step(w)
+    for kern, out in outs.items():
+        assert_parity(sp, out, ref)
+    # both families hold the 2e-3 bound; they also agree with each other
+    assert np.max(np.abs(outs[kb.KVD_KERNEL_MFMA] - outs[kb.KVD_KERNEL_VALU])) <= 4e-3 * np.max(np.abs(ref))
