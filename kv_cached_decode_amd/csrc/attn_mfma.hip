@@ -203,7 +203,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     int spec_blk = 0;
     // fused step: the frequency of this thread's rotation pair (pair
     // threadIdx.x % HALF in every round of the angle loop)
-    const double theta = FUSED ? a.theta.v[threadIdx.x % HALF] : 0.0;
+    const double theta = FUSED ? kernarg_double(offsetof(AttnArgs, theta), threadIdx.x % HALF) : 0.0;
     if (c.window == 0) {
         const long long skey = (long long)spec_base + (lane & 31);
         if (skey < ((long long)c.max_blocks << c.log2_bs))

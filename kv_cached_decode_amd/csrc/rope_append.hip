@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const int pos = local + (c.key_pos0 ? c.key_pos0[b] : 0);
     const int blk = c.table[(size_t)b * c.max_blocks + (local >> c.log2_bs)];
 
-    for (int p = threadIdx.x; p < half; p += blockDim.x) rope_angle(a.theta.v[p], pos, cs[p], sn[p]);
+    for (int p = threadIdx.x; p < half; p += blockDim.x)
+        rope_angle(kernarg_double(offsetof(RopeAppendArgs, theta), p), pos, cs[p], sn[p]);
     __syncthreads();
     if (!active) return;
 

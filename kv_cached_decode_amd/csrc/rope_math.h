@@ -11,6 +11,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+
 namespace kvd {
 
 // Element indices of pair i: HALF pairs (i, i + D/2), INTERLEAVED (2i, 2i+1).
@@ -25,6 +27,19 @@ __device__ inline void rope_pair(int i, int half, int interleaved, int& ia, int&
 __device__ inline void rope_angle(double theta, int pos, double& cs, double& sn) {
     const double phi = (double)pos * theta;
     sincos(phi, &sn, &cs);
+}
+
+// Element i (per thread) of a double table inside the kernel's by-value
+// argument block, read in place.  The explicit kernel arguments start at the
+// base of the kernarg segment (AMDGPU code-object ABI), so the table sits at
+// offsetof(Args, table) there.  Indexing the by-value argument itself with a
+// per-thread value would make the compiler copy the whole argument block to
+// scratch memory first.
+__device__ inline double kernarg_double(size_t table_offset, int i) {
+    typedef const __attribute__((address_space(4))) char kchar;
+    typedef const __attribute__((address_space(4))) double kdouble;
+    kchar* base = (kchar*)__builtin_amdgcn_kernarg_segment_ptr();
+    return ((kdouble*)(base + table_offset))[i];
 }
 
 // (x, y) turned by the angle whose cosine and sine are (c, s); no fused
