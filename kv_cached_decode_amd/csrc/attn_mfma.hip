@@ -38,6 +38,8 @@
 // sliding window, are masked the same way (causal within the draft).  Split
 // ranges start at the first key any query can see, so keys before every
 // window are not read.
+#include <type_traits>
+
 #include "bf16_round.h"
 #include "kvd_internal.h"
 #include "rope_math.h"
@@ -414,24 +416,26 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         int base = p0 + wave * TILE;
         if (base < p1 && !(spec && p0 == key_begin)) issue(base, p1, staged);
         if (p0 == key_begin) prepare_q();
-        for (; base < p1; base += STRIDE) {
-            if constexpr (FUSED) {
+        // One tile of the wave: scores, softmax, P.V, and the next tile's
+        // loads.  SUBST: the tile's loaded keys may include new tokens (the
+        // fused step's last tiles), whose rows are taken from LDS.
+        auto tile = [&](int base, auto subst) {
+            constexpr bool SUBST = decltype(subst)::value;
+            if constexpr (SUBST) {
                 // rows of new tokens (also where a clamped lane re-reads one)
                 // come from LDS, whatever the loads returned
-                if (min(base + TILE, p1) - 1 >= new0) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int key = min(base + 16 * h + n16, p1 - 1);
-                        if (key >= new0)
+                for (int h = 0; h < 2; ++h) {
+                    const int key = min(base + 16 * h + n16, p1 - 1);
+                    if (key >= new0)
 #pragma unroll
-                            for (int kk = 0; kk < 4; ++kk)
-                                kf[4 * h + kk] = *(const u32x4*)(sm_knew + (key - new0) * D + 32 * kk + 8 * j);
-                    }
+                        for (int kk = 0; kk < 4; ++kk)
+                            kf[4 * h + kk] = *(const u32x4*)(sm_knew + (key - new0) * D + 32 * kk + 8 * j);
+                }
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int key = min(base + 4 * i + j, p1 - 1);
-                        if (key >= new0) vf[i] = *(const u32x4*)(sm_vnew + (key - new0) * D + 8 * n16);
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    const int key = min(base + 4 * i + j, p1 - 1);
+                    if (key >= new0) vf[i] = *(const u32x4*)(sm_vnew + (key - new0) * D + 8 * n16);
                 }
             }
 #pragma unroll
@@ -490,7 +494,12 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
                 o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, o[nt], 0, 0, 0);
             }
             __builtin_amdgcn_wave_barrier();
-        }
+        };
+        // tiles before the first new token, then (fused step) the rest
+        for (; base < p1 && (!FUSED || min(base + TILE, p1) - 1 < new0); base += STRIDE)
+            tile(base, std::false_type{});
+        if constexpr (FUSED)
+            for (; base < p1; base += STRIDE) tile(base, std::true_type{});
         p0 = p1;
     }
 
