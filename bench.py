@@ -87,7 +87,7 @@ class Layers:
     def step(self, i):
         kv = self.kv[i % len(self.kv)]
         s = self.w.spec
-        kb.decode_step(kv, self.q, self.k, self.v, self.out, None, False, s.rope_base, s.layout, 0.0,
+        kb.decode_step(kv, self.q, self.k, self.v, self.out, self.q_rot, False, s.rope_base, s.layout, 0.0,
                        self.ws, self.num_splits, self.kernel)
 
     def two_calls(self, i):

@@ -88,8 +88,9 @@ __device__ inline float xor_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-// Sequence order: workgroups are dispatched in blockIdx order, so sequence
-// slot z of the grid takes the z-th longest sequence (ties by index).  With a
+// Sequence order: workgroups are dispatched in blockIdx order, so when the
+// grid is larger than the resident slots (the host says so), sequence slot z
+// of the grid takes the z-th longest sequence (ties by index).  With a
 // ragged batch the longest units start first and the short ones fill the
 // gaps (longest-processing-time-first list scheduling); a uniform batch keeps
 // its natural order.  Each thread ranks one sequence against all the others
@@ -215,7 +216,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     int L = c.seq_lens[z];
     int qo = q_local0(c, z, L);
     load_seq(z, L, qo);
-    if (c.B > 1 && c.B <= LPT_MAX_SEQS) {
+    if (a.rank_longest && c.B > 1 && c.B <= LPT_MAX_SEQS) {
         // the ranking borrows the V-tile LDS (unused until the key loop)
         int* sm_len = (int*)sm_v;
         for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];

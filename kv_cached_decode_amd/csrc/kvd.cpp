@@ -327,6 +327,8 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
     a.split_keys = p.split_keys;
     a.rows = p.rows;
     a.row_tile = p.row_tile;
+    // longest-first only pays when workgroups wait for a slot
+    a.rank_longest = (int64_t)p.splits * kv->n_kv_heads * kv->num_seqs > (int64_t)kvd::MFMA_WGS_PER_CU * num_cus();
     a.scale_log2 = (float)(scale * 1.4426950408889634);
     a.q = q_rot;
     a.out = out;

@@ -69,6 +69,7 @@ struct AttnArgs {
     int32_t split_keys;     // keys per split (multiple of the kernel's step)
     int32_t rows;           // g*T
     int32_t row_tile;       // rows handled by one workgroup (grid.y = Hkv * row tiles)
+    int32_t rank_longest;   // order sequences longest-first (the grid exceeds the resident slots)
     float scale_log2;       // softmax scale * log2(e)
     const float* q;         // [B][T][Hq][D]
     float* out;             // [B][T][Hq][D] (written directly when S == 1)
@@ -138,6 +139,8 @@ bool mfma_supported(int D, int kv_bf16, int rows);
 constexpr int PREFILL_ROWS = 64;
 int prefill_step_keys();
 int mfma_step_keys();
+// Workgroups of the decode matrix-core kernel resident on one CU.
+constexpr int MFMA_WGS_PER_CU = 2;
 // Resident workgroups per CU for a kernel variant (occupancy query on the
 // current device; a conservative default when there is none).
 int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds);
