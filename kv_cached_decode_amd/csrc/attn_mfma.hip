@@ -78,14 +78,23 @@ __device__ inline s16x4 lds_tr(const char* p) {
         (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
 }
 
+// Reductions over lanes l, l^16, l^32, l^48 (the four lane groups holding a
+// row's keys).  permlane16_swap / permlane32_swap of a register with itself
+// leave, in every lane, its own value and its partner's (lane ^ 16, lane ^ 32)
+// in the two results, in an order that depends on the lane; max and the
+// single addition are symmetric in them, so every lane gets the same value.
 __device__ inline float xor_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 __device__ inline float xor_sum(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 // Sequence order: workgroups are dispatched in blockIdx order, so when the

@@ -5,22 +5,29 @@
 // cache, head_dim 128.  Causal within the chunk: new token t sees the keys up
 // to its own position.
 //
-// Workgroup = 4 wave64s over a tile of 64 query rows of one (sequence, kv
-// head) -- wave w owns rows 16w .. 16w+15 of the tile, row r = t*g + hg --
-// and one key range (split).  Unlike the decode kernel, every wave needs
-// every key, so the K and V tiles (32 keys) are staged in LDS once by all 256
-// threads and shared by the four waves: the kv-head group's rows share the
-// keys, which is what makes the work dense enough for the matrix cores.
-// Double-buffered: while the waves consume tile i from LDS, each thread's
-// registers hold its share of tile i+1 on the way from HBM (one barrier per
-// tile).  Per wave and tile, as in the decode kernel:
+// Workgroup = 4 wave64s over a tile of 128 query rows of one (sequence, kv
+// head) -- wave w owns rows 32w .. 32w+31 of the tile as two 16-row blocks,
+// row r = t*g + hg -- and one key range (split).  Unlike the decode kernel,
+// every wave needs every key, so the K and V tiles (32 keys) are staged in
+// LDS once by all 256 threads and shared by the four waves: the kv-head
+// group's rows share the keys, which is what makes the work dense enough for
+// the matrix cores.  Each K or V operand a wave reads from LDS feeds both of
+// its row blocks, so LDS reads per query row are half those of one block per
+// wave.  Double-buffered: while the waves consume tile i from LDS, each
+// thread's registers hold its share of tile i+1 on the way from HBM (one
+// barrier per tile).  Per wave, row block and tile, as in the decode kernel:
 //   S^T[32 keys x 16 rows] = K . Q^T   (K from LDS, Q as bf16 hi + lo),
 //   online softmax per row (the row sits in lane l%16),
 //   O^T[128 x 16 rows] += V^T . P^T    (V^T read transposed from LDS, P as
 //   bf16 hi + lo).
-// The loop ends at the last key any row of the tile sees.  Split ranges,
-// windows, ragged chunks and context-parallel shards follow the same rules as
-// the decode kernels (kvd_internal.h).
+// The loop ends at the last key any row of the tile sees.  A wave skips the
+// tiles none of its rows sees (past the causal end of its last row, before
+// the window of its first), and leaves out the mask on tiles every one of its
+// rows sees whole; the running rescale happens only when a row's maximum
+// grows (otherwise its factor is exactly 1).  Rows past the chunk take no
+// part and write the empty result.  Split ranges, windows, ragged chunks and
+// context-parallel shards follow the same rules as the decode kernels
+// (kvd_internal.h).
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -34,13 +41,22 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int WAVES = 4;
 constexpr int D = 128;
 constexpr int TILE = 32;
-constexpr int ROWS = WAVES * 16;          // query rows per workgroup
+constexpr int RB = 2;                     // 16-row blocks per wave
+constexpr int WROWS = 16 * RB;            // query rows per wave
+constexpr int ROWS = WAVES * WROWS;       // query rows per workgroup
 constexpr int KROWB = D * 2 + 16;         // LDS row stride of the K tile: 16 rows read at one column hit distinct banks
 constexpr int VROWB = D * 2 + 32;         // LDS row stride of the V tile (transposed reads)
 constexpr int K_BYTES = TILE * KROWB;
 constexpr int V_BYTES = TILE * VROWB;
 constexpr int MAX_STAGED_BLOCKS = 4096;   // block ids of a split, staged in LDS
+constexpr int RANK_MAX = PREFILL_RANK_MAX;  // units ranked longest-first (their key counts and order share the block-id array)
+static_assert(2 * RANK_MAX <= MAX_STAGED_BLOCKS, "ranking arrays");
 constexpr float M_EMPTY = -1e30f;
+// The running maximum of a row moves (and its sums are rescaled) only when a
+// tile's scores exceed it by more than RESCALE_SLACK (log2 units); below that
+// the weights exp2(s - m) stay at most 2^RESCALE_SLACK, harmless in fp32, and
+// the result is the same since numerator and denominator share m.
+constexpr float RESCALE_SLACK = 8.0f;
 static_assert(ROWS == PREFILL_ROWS, "rows per workgroup");
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -58,76 +74,159 @@ __device__ inline s16x4 lds_tr(const char* p) {
         (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
 }
 
-__device__ inline float xor_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
-}
+// Reductions over lanes l, l^16, l^32, l^48 (the four lane groups holding a
+// row's keys).  permlane16_swap / permlane32_swap of a register with itself
+// leave, in every lane, its own value and its partner's (lane ^ 16, lane ^ 32)
+// in the two results, in an order that depends on the lane; max and the
+// single addition are symmetric in them, so every lane gets the same value.
+// (scores hold no NaN: a compare and select is the maximum)
+__device__ inline float max_sel(float a, float b) { return a > b ? a : b; }
 
 __device__ inline float xor_sum(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+__device__ inline float xor_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = max_sel(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max_sel(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// A unit of work is (sequence b, row tile, split): the keys
+// [key_begin, key_end) that rows row0 .. row0 + ROWS - 1 of the sequence's
+// kv-head group see within the split; live_rows of them are real (their
+// token is inside the chunk).  The same for every kv head.
+struct Unit {
+    int b, rtile, split;
+    int qo, n_live, key_begin, key_end, live_rows;
+};
+
+__device__ inline Unit unit_of(const AttnArgs& a, int u, int n_rtiles) {
+    const CacheView& c = a.c;
+    Unit w;
+    w.split = u % a.num_splits;
+    w.rtile = n_rtiles - 1 - (u / a.num_splits) % n_rtiles;   // later (longer) row tiles first
+    w.b = u / (a.num_splits * n_rtiles);
+    const int L = c.seq_lens[w.b];
+    const int nn = n_new(c, w.b);
+    w.qo = q_local0(c, w.b, L);
+    w.key_begin = range_start(c, w.qo) + w.split * a.split_keys;
+    const int row0 = w.rtile * ROWS;
+    w.n_live = nn * c.g;
+    w.live_rows = min(ROWS, w.n_live - row0);
+    // the last token of the tile inside the chunk sees keys up to its own position
+    const int t_last = min(nn, (row0 + ROWS - 1) / c.g + 1) - 1;
+    w.key_end = min(min(range_end(c, L, w.qo, nn), w.key_begin + a.split_keys), w.qo + t_last + 1);
+    return w;
 }
 
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char sm_k[2][K_BYTES];
     __shared__ __attribute__((aligned(16))) char sm_v[2][V_BYTES];
-    __shared__ int sm_blk[MAX_STAGED_BLOCKS];
+    __shared__ __attribute__((aligned(16))) int sm_blk[MAX_STAGED_BLOCKS];
 
     const CacheView& c = a.c;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15;
     const int j = lane >> 4;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y % c.Hkv;
-    const int rtile = blockIdx.y / c.Hkv;
-    const int b = blockIdx.z;
-    const int row0 = rtile * ROWS;
-
-    const int L = c.seq_lens[b];
-    const int nn = n_new(c, b);
-    const int qo = q_local0(c, b, L);
-    const int key_begin = range_start(c, qo) + split * a.split_keys;
-    // rows of this tile that are real (not past the chunk): t < nn
-    const int live_rows = min(ROWS, nn * c.g - row0);
-    // the last key a row of this tile sees
-    const int t_last = min(nn, (row0 + ROWS - 1) / c.g + 1) - 1;
-    const int key_end = min(min(range_end(c, L, qo, nn), key_begin + a.split_keys), qo + t_last + 1);
+    // Grid: kv head fastest (consecutive workgroups, one per kv head, read
+    // different heads' keys), then the unit position.
+    const int kvh = blockIdx.x % c.Hkv;
+    const int pos = blockIdx.x / c.Hkv;
+    const int n_rtiles = (a.rows + ROWS - 1) / ROWS;
+    const int n_units = a.num_splits * n_rtiles * c.B;
+    int u = pos;
+    if (a.rank_longest && n_units <= RANK_MAX) {
+        // Longest-first: position pos takes the unit of rank pos by key count
+        // (ties by unit index; empty units last), so the longest units start
+        // first and the short ones fill the slots at the end.  Every
+        // workgroup derives the same permutation.
+        int* const sm_work = sm_blk;
+        int* const sm_perm = sm_blk + RANK_MAX;
+        const int n4 = (n_units + 3) & ~3;
+        for (int v = tid; v < n4; v += blockDim.x) {
+            int w = -1;        // padding: below every unit
+            if (v < n_units) {
+                const Unit x = unit_of(a, v, n_rtiles);
+                w = x.live_rows > 0 ? max(0, x.key_end - x.key_begin) : 0;
+            }
+            sm_work[v] = w;
+        }
+        __syncthreads();
+        for (int v = tid; v < n_units; v += blockDim.x) {
+            const int w = sm_work[v];
+            int r = 0;
+            for (int i = 0; i < n4; i += 4) {
+                const int4 x = *(const int4*)(sm_work + i);
+                r += (x.x > w) + (x.y > w) + (x.z > w) + (x.w > w);
+                r += (x.x == w && i + 0 < v) + (x.y == w && i + 1 < v) + (x.z == w && i + 2 < v) +
+                     (x.w == w && i + 3 < v);
+            }
+            sm_perm[r] = v;
+        }
+        __syncthreads();
+        u = sm_perm[pos];
+        __syncthreads();       // sm_blk is reused for block ids below
+    }
+    const Unit un = unit_of(a, u, n_rtiles);
+    const int b = un.b, split = un.split;
+    const int row0 = un.rtile * ROWS;
+    const int qo = un.qo, n_live = un.n_live, live_rows = un.live_rows;
+    const int key_begin = un.key_begin, key_end = un.key_end;
     if (live_rows <= 0 || key_begin >= key_end) {
         write_empty_partials(a, b, kvh, split, row0, ROWS);
         return;
     }
 
-    // this lane's query row (within the wave's 16) and its visible keys
-    const int row = row0 + 16 * wave + n16;
-    const bool row_ok = row < a.rows;
-    const bool row_live = row_ok && row < nn * c.g;
-    const int t_row = row_ok ? row / c.g : 0;
-    const int h_row = kvh * c.g + (row_ok ? row - t_row * c.g : 0);
-    const int vis = row_live ? qo + t_row : -1;
-    const int lo = c.window > 0 ? vis - c.window + 1 : 0;
+    // The wave's rows wrow0 .. wrow0 + 31, the live ones up to wlast: keys a
+    // live row of the wave sees lie in [lo_min, vis_last]; every one of them
+    // sees [lo_max, vis_first].
+    const int wrow0 = row0 + WROWS * wave;
+    const bool wave_live = wrow0 < n_live;
+    const int wlast = min(wrow0 + WROWS, n_live) - 1;
+    const int vis_first = qo + wrow0 / c.g;
+    const int vis_last = qo + wlast / c.g;
+    const int lo_min = vis_first - c.window + 1;
+    const int lo_max = vis_last - c.window + 1;
 
-    // Q^T operand (dims 32kk + 8j .. +8 of the row) in log2 units, hi + lo
-    bf16x8 qhi[4], qlo[4];
-    {
-        const float* qp = a.q + (((size_t)b * c.T + t_row) * c.Hq + h_row) * D;
+    // this lane's query rows (row n16 of each block) and their visible keys
+    bool row_ok[RB], row_live[RB];
+    int vis[RB], lo[RB];
+    size_t qrow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = wrow0 + 16 * rb + n16;
+        row_ok[rb] = row < a.rows;
+        row_live[rb] = row < n_live;             // n_live <= rows
+        const int t = row_ok[rb] ? row / c.g : 0;
+        qrow[rb] = ((size_t)b * c.T + t) * c.Hq + kvh * c.g + (row_ok[rb] ? row - t * c.g : 0);
+        vis[rb] = row_live[rb] ? qo + t : -1;
+        lo[rb] = c.window > 0 ? vis[rb] - c.window + 1 : 0;
+    }
+
+    // This lane's query elements (dims 32kk + 8j .. +8 of each row; rows past
+    // the chunk take zeros, their results are replaced below) and the
+    // split's block ids are fetched together; the first K/V tile's loads go
+    // out once the block ids are in LDS.
+    float4 xq[RB][4][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float* qp = a.q + qrow[rb] * D;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const float4 x0 = *(const float4*)(qp + 32 * kk + 8 * j);
-            const float4 x1 = *(const float4*)(qp + 32 * kk + 8 * j + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = row_ok ? xs[e] * a.scale_log2 : 0.0f;
-                const __bf16 hi = (__bf16)v;
-                qhi[kk][e] = hi;
-                qlo[kk][e] = (__bf16)(v - (float)hi);
+            xq[rb][kk][0] = xq[rb][kk][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (row_live[rb]) {
+                xq[rb][kk][0] = *(const float4*)(qp + 32 * kk + 8 * j);
+                xq[rb][kk][1] = *(const float4*)(qp + 32 * kk + 8 * j + 4);
             }
         }
     }
-
-    // block ids of [key_begin, key_end)
     const int blk0 = key_begin >> c.log2_bs;
     const int nblk = ((key_end - 1) >> c.log2_bs) - blk0 + 1;
     const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
@@ -160,69 +259,127 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
             *(u32x4*)(sm_v[buf] + (ch >> 4) * VROWB + 16 * (ch & 15)) = vr[i];
         }
     };
-
-    float m = M_EMPTY, lsum = 0.0f;
-    f32x4 o[8];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-
     load(key_begin);
+
+    // Q^T operands in log2 units, hi + lo
+    bf16x8 qhi[RB][4], qlo[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float4 x0 = xq[rb][kk][0], x1 = xq[rb][kk][1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = xs[e] * a.scale_log2;
+                const __bf16 hi = (__bf16)v;
+                qhi[rb][kk][e] = hi;
+                qlo[rb][kk][e] = (__bf16)(v - (float)hi);
+            }
+        }
+
+    // running max m (log2 units), O^T and this lane's part of the row sums
+    float m[RB], lsum[RB];
+    f32x4 o[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m[rb] = M_EMPTY;
+        lsum[rb] = 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
     stage(0);
     __syncthreads();
     if (key_begin + TILE < key_end) load(key_begin + TILE);
 
     int buf = 0;
     for (int base = key_begin; base < key_end; base += TILE, buf ^= 1) {
-        const char* kt = sm_k[buf];
-        const char* vt = sm_v[buf];
-        // scores: S^T tiles (16 keys x 16 rows), keys base + 16h + 4j + i
-        f32x4 s[2];
+        // wave-uniform: does any live row of the wave see a key of the tile,
+        // and does every one see all of them?
+        const bool active = wave_live && base <= vis_last && (c.window == 0 || base + TILE - 1 >= lo_min);
+        if (active) {
+            const bool whole = base + TILE <= key_end && base + TILE - 1 <= vis_first &&
+                               (c.window == 0 || base >= lo_max);
+            const char* kt = sm_k[buf];
+            const char* vt = sm_v[buf];
+            // scores: S^T tiles (16 keys x 16 rows), keys base + 16h + 4j + i
+            f32x4 s[RB][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            const char* kp = kt + (16 * h + n16) * KROWB + 16 * j;
+            for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 kop = as_bf16x8(*(const u32x4*)(kp + 64 * kk));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[kk], acc, 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb) s[rb][h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+                const char* kp = kt + (16 * h + n16) * KROWB + 16 * j;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x8 kop = as_bf16x8(*(const u32x4*)(kp + 64 * kk));
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        s[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[rb][kk], s[rb][h], 0, 0, 0);
+                        s[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[rb][kk], s[rb][h], 0, 0, 0);
+                    }
+                }
             }
-            s[h] = acc;
-        }
-        // mask, running max, weights
-        float mx = m;
+            if (!whole) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = base + 16 * h + 4 * j + i;
-                if (key >= key_end || key > vis || key < lo) s[h][i] = -INFINITY;
-                mx = fmaxf(mx, s[h][i]);
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int key = base + 16 * h + 4 * j + i;
+                            if (key >= key_end || key > vis[rb] || key < lo[rb]) s[rb][h][i] = -INFINITY;
+                        }
             }
-        mx = xor_max(mx);
-        const float alpha = fast_exp2(m - mx);
-        m = mx;
-        lsum *= alpha;
+            // running maxima: every row moves to its maximum when one row
+            // of the wave grew past the slack
+            float mx[RB];
+            bool grew = false;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
-        bf16x8 phi, plo;
+            for (int rb = 0; rb < RB; ++rb) {
+                float x = m[rb];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[h][i] - m);
-                lsum += p;
-                const __bf16 hi = (__bf16)p;
-                phi[4 * h + i] = hi;
-                plo[4 * h + i] = (__bf16)(p - (float)hi);
+                    for (int i = 0; i < 4; ++i) x = max_sel(x, s[rb][h][i]);
+                mx[rb] = xor_max(x);
+                grew |= mx[rb] > m[rb] + RESCALE_SLACK;
             }
-        // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i and 16 + 4j + i
-        const char* rd = vt + (4 * j + (n16 >> 2)) * VROWB + 8 * (n16 & 3);
+            if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * VROWB + 32 * nt));
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, o[nt], 0, 0, 0);
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, o[nt], 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float alpha = fast_exp2(m[rb] - mx[rb]);
+                    m[rb] = mx[rb];
+                    lsum[rb] *= alpha;
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= alpha;
+                }
+            }
+            bf16x8 phi[RB], plo[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float p = fast_exp2(s[rb][h][i] - m[rb]);
+                        lsum[rb] += p;
+                        const __bf16 hi = (__bf16)p;
+                        phi[rb][4 * h + i] = hi;
+                        plo[rb][4 * h + i] = (__bf16)(p - (float)hi);
+                    }
+            // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i and 16 + 4j + i
+            const char* rd = vt + (4 * j + (n16 >> 2)) * VROWB + 8 * (n16 & 3);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * VROWB + 32 * nt));
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[rb], o[rb][nt], 0, 0, 0);
+                    o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[rb], o[rb][nt], 0, 0, 0);
+                }
+            }
+
         }
         // the next tile into the other buffer (read two tiles ago, released
         // by the last barrier), then the one after it from HBM
@@ -232,26 +389,35 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     }
 
     // row n16's sum over the four lane groups; O^T element (dim 16nt + 4j + i, row n16)
-    lsum = xor_sum(lsum);
-    if (!row_ok) return;
-    const int t = t_row;
-    const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h_row;
-    if (a.num_splits == 1) {
-        float* op = a.out + qrow * D;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            *(float4*)(op + 16 * nt + 4 * j) = make_float4(finish_out(o[nt][0], lsum), finish_out(o[nt][1], lsum),
-                                                           finish_out(o[nt][2], lsum), finish_out(o[nt][3], lsum));
-        if (a.lse && j == 0) a.lse[qrow] = finish_lse(m, lsum);
-    } else {
-        const size_t part = qrow * a.num_splits + split;
-        float* op = a.part_o + part * D;
+    for (int rb = 0; rb < RB; ++rb) lsum[rb] = xor_sum(lsum[rb]);   // all lanes active
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            *(float4*)(op + 16 * nt + 4 * j) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
-        if (j == 0) {
-            a.part_ml[part * 2 + 0] = m;
-            a.part_ml[part * 2 + 1] = lsum;
+    for (int rb = 0; rb < RB; ++rb) {
+        if (!row_ok[rb]) continue;
+        if (!row_live[rb]) {        // a padding token: the empty result
+            m[rb] = M_EMPTY;
+            lsum[rb] = 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (a.num_splits == 1) {
+            float* op = a.out + qrow[rb] * D;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                *(float4*)(op + 16 * nt + 4 * j) =
+                    make_float4(finish_out(o[rb][nt][0], lsum[rb]), finish_out(o[rb][nt][1], lsum[rb]),
+                                finish_out(o[rb][nt][2], lsum[rb]), finish_out(o[rb][nt][3], lsum[rb]));
+            if (a.lse && j == 0) a.lse[qrow[rb]] = finish_lse(m[rb], lsum[rb]);
+        } else {
+            const size_t part = qrow[rb] * a.num_splits + split;
+            float* op = a.part_o + part * D;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                *(float4*)(op + 16 * nt + 4 * j) = make_float4(o[rb][nt][0], o[rb][nt][1], o[rb][nt][2], o[rb][nt][3]);
+            if (j == 0) {
+                a.part_ml[part * 2 + 0] = m[rb];
+                a.part_ml[part * 2 + 1] = lsum[rb];
+            }
         }
     }
 }
@@ -261,8 +427,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 int prefill_step_keys() { return TILE; }
 
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s) {
-    const int n_rtiles = (a.rows + ROWS - 1) / ROWS;
-    dim3 grid(a.num_splits, a.c.Hkv * n_rtiles, a.c.B);
+    const int64_t n_rtiles = (a.rows + ROWS - 1) / ROWS;
+    const int64_t n = (int64_t)a.num_splits * n_rtiles * a.c.B * a.c.Hkv;
+    if (n > INT32_MAX) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)n);
     hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -151,7 +151,7 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     if (kernel != KVD_KERNEL_AUTO && kernel != KVD_KERNEL_VALU && kernel != KVD_KERNEL_MFMA)
         return fail(KVD_ERR_UNSUPPORTED, "kernel = %d", kernel);
     // the matrix-core kernels: the decode kernel up to 16 query rows per kv
-    // head, the prefill kernel (64-row tiles sharing LDS-staged K/V) beyond
+    // head, the prefill kernel (128-row tiles sharing LDS-staged K/V) beyond
     const bool mfma_ok = kvd::mfma_supported(D, bf16, 1);
     if (kernel == KVD_KERNEL_MFMA && !mfma_ok)
         return fail(KVD_ERR_UNSUPPORTED, "matrix-core kernels need a bf16 cache and head_dim 128");
@@ -209,7 +209,11 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     int64_t keys = cdiv(max_len, splits);
     splits = cdiv(max_len, keys);
     if (splits > 65535) return fail(KVD_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)splits);
-    if ((int64_t)kv->n_kv_heads * n_rtiles > 65535 || kv->num_seqs > 65535)
+    if (p->prefill) {
+        if (splits * kv->n_kv_heads * n_rtiles * kv->num_seqs > INT32_MAX)
+            return fail(KVD_ERR_UNSUPPORTED, "grid too large: %lld splits x %d kv heads x %d row tiles x %d sequences",
+                        (long long)splits, kv->n_kv_heads, n_rtiles, kv->num_seqs);
+    } else if ((int64_t)kv->n_kv_heads * n_rtiles > 65535 || kv->num_seqs > 65535)
         return fail(KVD_ERR_UNSUPPORTED, "grid too large: %d kv heads x %d row tiles, %d sequences",
                     kv->n_kv_heads, n_rtiles, kv->num_seqs);
     p->splits = (int)splits;
@@ -328,7 +332,12 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
     a.rows = p.rows;
     a.row_tile = p.row_tile;
     // longest-first only pays when workgroups wait for a slot
-    a.rank_longest = (int64_t)p.splits * kv->n_kv_heads * kv->num_seqs > (int64_t)kvd::MFMA_WGS_PER_CU * num_cus();
+    if (p.prefill) {
+        const int64_t units = (int64_t)p.splits * cdiv(p.rows, kvd::PREFILL_ROWS) * kv->num_seqs;
+        a.rank_longest = units <= kvd::PREFILL_RANK_MAX && units * kv->n_kv_heads > 2 * (int64_t)num_cus();
+    } else {
+        a.rank_longest = (int64_t)p.splits * kv->n_kv_heads * kv->num_seqs > (int64_t)kvd::MFMA_WGS_PER_CU * num_cus();
+    }
     a.scale_log2 = (float)(scale * 1.4426950408889634);
     a.q = q_rot;
     a.out = out;

@@ -69,7 +69,7 @@ struct AttnArgs {
     int32_t split_keys;     // keys per split (multiple of the kernel's step)
     int32_t rows;           // g*T
     int32_t row_tile;       // rows handled by one workgroup (grid.y = Hkv * row tiles)
-    int32_t rank_longest;   // order sequences longest-first (the grid exceeds the resident slots)
+    int32_t rank_longest;   // order work longest-first (the grid exceeds the resident slots)
     float scale_log2;       // softmax scale * log2(e)
     const float* q;         // [B][T][Hq][D]
     float* out;             // [B][T][Hq][D] (written directly when S == 1)
@@ -136,7 +136,10 @@ constexpr int VALU_MAX_STAGED_BLOCKS = 4096;
 int valu_max_split_keys(int log2_bs);
 bool mfma_supported(int D, int kv_bf16, int rows);
 // Query rows of one prefill workgroup (more rows than the decode kernel takes).
-constexpr int PREFILL_ROWS = 64;
+constexpr int PREFILL_ROWS = 128;
+// Prefill grids of at most this many (sequence, row tile, split) units are
+// ordered longest-first inside the kernel.
+constexpr int PREFILL_RANK_MAX = 256;
 int prefill_step_keys();
 int mfma_step_keys();
 // Workgroups of the decode matrix-core kernel resident on one CU.

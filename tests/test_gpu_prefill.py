@@ -100,3 +100,23 @@ def test_prefill_and_valu_kernels_agree():
         assert_parity(sp, out, ref)
     # both families hold the 2e-3 bound; they also agree with each other
     assert np.max(np.abs(outs[kb.KVD_KERNEL_MFMA] - outs[kb.KVD_KERNEL_VALU])) <= 4e-3 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("splits", [0, 2])
+def test_longest_first_unit_order(splits):
+    """More (sequence, row tile, split) units than resident workgroup slots,
+    ragged chunks with empty tiles: the kernel takes its units longest-first
+    (a permutation every workgroup derives); every row still matches."""
+    sp = spec("ranked_units", 12, 256, 32, 8, (0, 300), 70, chunk=(1, 256))
+    w = workloads.make_workload(sp)
+    note("longest-first", splits, "q_lens", w.q_lens.tolist())
+    case = GpuCase(w)
+    plan = kb.decode_attention_plan(case.kv, num_splits=splits)
+    # 8 row tiles x 12 sequences x splits units, 8 kv heads each: beyond the
+    # 2 x 256 resident slots
+    assert plan[2] == kb.KVD_KERNEL_MFMA and plan[0] == (splits or 1)
+    _, out = case.step(num_splits=splits)
+    _, ref, _, _ = oracle_step(w)
+    for b, n in enumerate(w.q_lens):
+        assert np.all(out[b, n:] == 0.0), "padding rows must be 0"
+    assert_parity(sp, out, ref)
