@@ -391,14 +391,14 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // first tile is issued (whose registers its fp64 work would compete
     // with) and before the first piece (whose barriers also publish the new
     // K/V rows in LDS).
+    const bool spec = c.window == 0 && b == z && spec_base < first_p1;
+    if (spec) issue(spec_base, first_p1, [&](int key) { return __shfl(spec_blk, key - spec_base); });
     if constexpr (FUSED) {
         fused_angles();
         __syncthreads();
         fused_rotate_q();
         fused_append();
     }
-    const bool spec = c.window == 0 && b == z && spec_base < first_p1;
-    if (spec) issue(spec_base, first_p1, [&](int key) { return __shfl(spec_blk, key - spec_base); });
 
     // pieces of at most MAX_PIECE_BLOCKS cache blocks (block ids in LDS)
     for (int p0 = key_begin; p0 < key_end;) {
