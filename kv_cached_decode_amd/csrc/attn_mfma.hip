@@ -30,8 +30,11 @@
 // in fp64 into LDS, the same arithmetic as the stand-alone RoPE kernel); the
 // workgroup whose key range holds new tokens rotates and rounds their K/V
 // rows, stores them into the cache and substitutes them into its own tiles
-// from LDS, so it never waits for its own stores.  The result is bitwise the
-// RoPE/append kernel followed by the unfused attention with the same plan.
+// from LDS, so it never waits for its own stores.  The rotated queries, when
+// the caller wants them, are written after the key loop: stores issued with
+// the first tile in flight are waited for together with it (one in-order
+// memory counter).  The result is bitwise the RoPE/append kernel followed by
+// the unfused attention with the same plan.
 //
 // Keys past the range are clamped to the range's last key for the loads and
 // masked to weight 0; keys past a draft token's position, or before its
@@ -58,7 +61,7 @@ constexpr int TILE = 32;                 // keys per wave iteration
 constexpr int ROWB = D * 2 + 32;         // LDS row stride of the V tile (bytes)
 constexpr int VT_BYTES = TILE * ROWB;    // one wave's V tile
 constexpr float M_EMPTY = -1e30f;
-constexpr int MAX_PIECE_BLOCKS = 2048;   // block ids staged in LDS at a time
+constexpr int MAX_PIECE_BLOCKS = MFMA_PIECE_BLOCKS;   // block ids staged in LDS at a time
 constexpr int LPT_MAX_SEQS = 256;        // batches ranked longest-first (one rank per thread)
 constexpr int MAX_T = 16;                // new tokens per sequence (rows <= 16)
 constexpr int HALF = D / 2;
@@ -129,15 +132,16 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     __shared__ float sm_l[WAVES][16];
     __shared__ int sm_pick;
     // fused step: the rounded new K/V rows ([t][dim], bf16 bits), read by the
-    // key loop; before the loop the V-tile area holds, after the sequence
-    // lengths of the longest-first ranking, the cos/sin of the new positions'
-    // angles ([t][pair]) and the query rows being rotated
+    // key loop; the query rows, raw then rotated (written to q_rot after the
+    // loop); before the loop the V-tile
+    // area holds, after the sequence lengths of the longest-first ranking,
+    // the cos/sin of the new positions' angles ([t][pair])
     __shared__ __attribute__((aligned(16))) uint16_t sm_knew[FUSED ? MAX_T * D : 8];
     __shared__ __attribute__((aligned(16))) uint16_t sm_vnew[FUSED ? MAX_T * D : 8];
+    __shared__ __attribute__((aligned(16))) float sm_q[FUSED ? 16 * D : 4];
     double* const sm_cs = (double*)(sm_v + LPT_MAX_SEQS * 4);   // past the ranking's lengths
     double* const sm_sn = sm_cs + MAX_T * HALF;
-    float* const sm_q = (float*)(sm_sn + MAX_T * HALF);
-    static_assert(LPT_MAX_SEQS * 4 + 2 * MAX_T * HALF * 8 + 16 * D * 4 <= WAVES * VT_BYTES,
+    static_assert(LPT_MAX_SEQS * 4 + 2 * MAX_T * HALF * 8 <= WAVES * VT_BYTES,
                   "fused scratch must fit in the V tiles");
     float (*sm_o)[16][D + 1] = (float (*)[16][D + 1])sm_v;
 
@@ -154,16 +158,17 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     const int t_row = row_ok ? row / c.g : 0;
     const int h_row = kvh * c.g + (row_ok ? row - t_row * c.g : 0);
 
-    // Loads that depend on the sequence: its length, this lane's q slice and
-    // the block ids of the split's first piece (one per thread).  They are
-    // issued for slot z before the longest-first ranking is known -- the
-    // ranking keeps uniform batches in place -- and redone if it moves z.
+    // Loads that depend on the sequence: this lane's q slice (in the fused
+    // step only wave 0's: it lays out the rows that every wave rotates), the
+    // block ids of the split's first piece (thread i: ids i, i + 256, ...)
+    // and, in the fused step, this thread's first new-key pair.  Without a
+    // window, and when no longest-first ranking picks the sequence, none of
+    // them needs the sequence's length: they go out together with it, one
+    // memory round trip for all.  Otherwise they follow the length (and the
+    // ranking).
     float xq[4][8];
-    int tb = 0;
-    // fused step: this thread's first new-key pair (k pair, v pair) and the
-    // block it goes to, if the split holds new tokens
+    int tb[MAX_PIECE_BLOCKS / 256];
     float kx = 0.0f, ky = 0.0f, vx = 0.0f, vy = 0.0f;
-    int kblk = 0;
     // qo: local index of the position of the sequence's first new token
     auto split_begin = [&](int qo) { return range_start(c, qo) + split * a.split_keys; };
     auto new_pair = [&](int bb, int qo, int idx, int& ia, int& ic, size_t& src) {
@@ -172,24 +177,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         rope_pair(idx % HALF, HALF, a.interleaved, ia, ic);
         src = (((size_t)bb * c.T + t) * c.Hkv + kvh) * D;
     };
-    auto load_seq = [&](int bb, int LL, int qo) {
-        const int key_begin = split_begin(qo);
-        const int rend = range_end(c, LL, qo, n_new(c, bb));
-        if constexpr (FUSED) {
-            const int n0 = max(qo, key_begin);
-            const int n1 = min(rend, key_begin + a.split_keys);
-            if ((int)threadIdx.x < (n1 - n0) * HALF) {
-                int ia, ic;
-                size_t src;
-                new_pair(bb, qo, threadIdx.x, ia, ic, src);
-                const int i = threadIdx.x % HALF;
-                kx = a.k_new[src + ia];
-                ky = a.k_new[src + ic];
-                vx = a.v_new[src + 2 * i];
-                vy = a.v_new[src + 2 * i + 1];
-                kblk = c.table[(size_t)bb * c.max_blocks + ((n0 + (int)threadIdx.x / HALF) >> c.log2_bs)];
-            }
-        }
+    auto load_q = [&](int bb) {
+        if (FUSED && wave != 0) return;
         const float* qp = a.q + (((size_t)bb * c.T + t_row) * c.Hq + h_row) * D;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -198,45 +187,66 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             xq[kk][0] = x0.x; xq[kk][1] = x0.y; xq[kk][2] = x0.z; xq[kk][3] = x0.w;
             xq[kk][4] = x1.x; xq[kk][5] = x1.y; xq[kk][6] = x1.z; xq[kk][7] = x1.w;
         }
-        if (key_begin < rend) {
-            const int blk0 = key_begin >> c.log2_bs;
-            const int last = min(rend, key_begin + a.split_keys) - 1;
-            const int nblk = min((last >> c.log2_bs) - blk0 + 1, MAX_PIECE_BLOCKS);
-            if ((int)threadIdx.x < nblk) tb = c.table[(size_t)bb * c.max_blocks + blk0 + threadIdx.x];
+    };
+    // block ids from the one holding key kb0 on, inside the table row, as
+    // many as a split can span
+    const int span = min(MAX_PIECE_BLOCKS, ((a.split_keys + (1 << c.log2_bs) - 2) >> c.log2_bs) + 1);
+    auto load_blocks = [&](int bb, int kb0) {
+        const int* trow = c.table + (size_t)bb * c.max_blocks;
+        const int blk0 = kb0 >> c.log2_bs;
+#pragma unroll
+        for (int r = 0; r < MAX_PIECE_BLOCKS / 256; ++r) {
+            const int i = (int)threadIdx.x + 256 * r;
+            tb[r] = i < span && blk0 + i < c.max_blocks ? trow[blk0 + i] : 0;
         }
     };
-    // Without a window a split's first key does not depend on the sequence
-    // length, so each lane fetches the block id of one key of its wave's
-    // first tile (lanes 32..63 repeat 0..31) together with the length: if
-    // the ranking below keeps this workgroup on sequence z, the first tile
-    // is issued from these ids, one memory round trip sooner.  The read stays
+    // fused step: pair threadIdx.x % HALF of new token t0 + threadIdx.x / HALF
+    auto load_new_pair = [&](int bb, int t0) {
+        if constexpr (FUSED) {
+            const int t = t0 + (int)threadIdx.x / HALF;
+            if (t >= 0 && t < c.T) {
+                int ia, ic;
+                rope_pair(threadIdx.x % HALF, HALF, a.interleaved, ia, ic);
+                const size_t src = (((size_t)bb * c.T + t) * c.Hkv + kvh) * D;
+                const int i = threadIdx.x % HALF;
+                kx = a.k_new[src + ia];
+                ky = a.k_new[src + ic];
+                vx = a.v_new[src + 2 * i];
+                vy = a.v_new[src + 2 * i + 1];
+            }
+        }
+    };
+    // In the same case each lane also fetches the block id of one key of its
+    // wave's first tile (lanes 32..63 repeat 0..31), and the first tile is
+    // issued from these ids before anything else waits.  The reads stay
     // inside the table row.
+    const bool ranked = a.rank_longest && c.B > 1 && c.B <= LPT_MAX_SEQS;
+    const bool early = c.window == 0 && !ranked;
     const int spec_base = split * a.split_keys + wave * TILE;
     int spec_blk = 0;
     // fused step: the frequency of this thread's rotation pair (pair
     // threadIdx.x % HALF in every round of the angle loop)
     const double theta = FUSED ? kernarg_double(offsetof(AttnArgs, theta), threadIdx.x % HALF) : 0.0;
-    if (c.window == 0) {
+    if (early) {
         const long long skey = (long long)spec_base + (lane & 31);
         if (skey < ((long long)c.max_blocks << c.log2_bs))
             spec_blk = c.table[(size_t)z * c.max_blocks + (int)(skey >> c.log2_bs)];
+        load_blocks(z, split * a.split_keys);
+        load_q(z);
+        load_new_pair(z, 0);
     }
     int b = z;
     int L = c.seq_lens[z];
-    int qo = q_local0(c, z, L);
-    load_seq(z, L, qo);
-    if (a.rank_longest && c.B > 1 && c.B <= LPT_MAX_SEQS) {
+    if (ranked) {
         // the ranking borrows the V-tile LDS (unused until the key loop)
         int* sm_len = (int*)sm_v;
         for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];
         __syncthreads();
         b = lpt_rank_pick(c.B, z, sm_len, &sm_pick);
-        if (b != z) {
-            L = sm_len[b];
-            qo = q_local0(c, b, L);
-            load_seq(b, L, qo);
-        }
+        L = sm_len[b];
     }
+    const int qo = q_local0(c, b, L);
+    if (!early) load_q(b);
     const int nn = n_new(c, b);          // new tokens of this sequence (rows past them: padding)
     const int key_begin = split_begin(qo);
     const int rend = range_end(c, L, qo, nn);
@@ -245,6 +255,10 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         return;
     }
     const int key_end = min(rend, key_begin + a.split_keys);
+    if (!early) load_blocks(b, key_begin);
+    // first new token this split holds (if any): the early pair assumed 0
+    const int t0 = max(qo, key_begin) - qo;
+    if (!early || t0 != 0) load_new_pair(b, t0);
     const bool row_live = row_ok && t_row < nn;
     const int vis = row_live ? qo + t_row : -1;            // last key this row sees
     const int lo = c.window > 0 ? vis - c.window + 1 : 0;  // first key it sees
@@ -275,11 +289,9 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         for (int idx = threadIdx.x; idx < c.T * HALF; idx += blockDim.x)
             rope_angle(theta, new0 + idx / HALF, sm_cs[idx], sm_sn[idx]);
     };
-    auto fused_rotate_q = [&]() {
-        // this lane's raw slice of its row into LDS (every wave holds the
-        // same rows; wave 0 stores them), then one pair per thread, then each
-        // lane takes its rotated slice back (rotated per lane, the sixteen
-        // pairs' fp64 temporaries would not fit beside the first loads)
+    // wave 0's raw slices of the rows into LDS (every wave holds the same
+    // rows); the rotation reads them after the barrier that follows the angles
+    auto fused_stage_q = [&]() {
         if (wave == 0 && row_ok) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -288,7 +300,11 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
                 *(float4*)(qs + 4) = make_float4(xq[kk][4], xq[kk][5], xq[kk][6], xq[kk][7]);
             }
         }
-        __syncthreads();
+    };
+    auto fused_rotate_q = [&]() {
+        // one pair per thread, then each lane takes its rotated slice back
+        // (rotated per lane, the sixteen pairs' fp64 temporaries would not
+        // fit beside the first loads)
         for (int idx = threadIdx.x; idx < a.rows * HALF; idx += blockDim.x) {
             const int r = idx / HALF, i = idx % HALF, t = r / c.g;
             int ia, ic;
@@ -298,11 +314,6 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             const float x1 = (float)xr, y1 = (float)yr;
             sm_q[r * D + ia] = x1;
             sm_q[r * D + ic] = y1;
-            if (a.q_rot && split == 0 && t < nn) {
-                float* qr = a.q_rot + (((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g)) * D;
-                qr[ia] = x1;
-                qr[ic] = y1;
-            }
         }
         __syncthreads();
         if (row_ok) {
@@ -317,28 +328,23 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     };
     auto fused_append = [&]() {
         // new keys n0 .. key_end-1 of this split (none unless it holds the
-        // tail); the first pair of each thread, and its block id, were loaded
-        // with q
+        // tail): pair idx goes to key n0 + idx / HALF.  The first pair of
+        // each thread was loaded with q (a later round loads its own, so the
+        // first round waits for nothing).
         const int n0 = max(new0, key_begin);
         if (key_end <= n0) return;
+        const int count = (key_end - n0) * HALF;
         uint16_t* kc = (uint16_t*)c.k;
         uint16_t* vc = (uint16_t*)c.v;
-        for (int idx = threadIdx.x; idx < (key_end - n0) * HALF; idx += blockDim.x) {
+        auto put = [&](int idx, int ia, int ic, float x0, float x1, float w0, float w1) {
             const int key = n0 + idx / HALF, i = idx % HALF, t = key - new0;
-            int ia, ic;
-            size_t src;
-            new_pair(b, qo, idx, ia, ic, src);
-            if (idx >= (int)blockDim.x) {
-                kx = a.k_new[src + ia];
-                ky = a.k_new[src + ic];
-                vx = a.v_new[src + 2 * i];
-                vy = a.v_new[src + 2 * i + 1];
-                kblk = c.table[(size_t)b * c.max_blocks + (key >> c.log2_bs)];
-            }
             double xr, yr;
-            rope_rotate(kx, ky, sm_cs[t * HALF + i], sm_sn[t * HALF + i], xr, yr);
+            rope_rotate(x0, x1, sm_cs[t * HALF + i], sm_sn[t * HALF + i], xr, yr);
             const uint16_t k0 = bf16_from_f64(xr), k1 = bf16_from_f64(yr);
-            const uint16_t v0 = bf16_from_f32(vx), v1 = bf16_from_f32(vy);
+            const uint16_t v0 = bf16_from_f32(w0), v1 = bf16_from_f32(w1);
+            // the host fuses only splits of at most MAX_PIECE_BLOCKS blocks,
+            // so the staged block ids are the whole split's
+            const int kblk = sm_blk[(key >> c.log2_bs) - (key_begin >> c.log2_bs)];
             const size_t dst = ((((size_t)kblk * c.Hkv + kvh) << c.log2_bs) + (key & ((1 << c.log2_bs) - 1))) * D;
             kc[dst + ia] = k0;
             kc[dst + ic] = k1;
@@ -348,6 +354,18 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             sm_knew[t * D + ic] = k1;
             sm_vnew[t * D + 2 * i] = v0;
             sm_vnew[t * D + 2 * i + 1] = v1;
+        };
+        if ((int)threadIdx.x < count) {
+            int ia, ic;
+            rope_pair(threadIdx.x % HALF, HALF, a.interleaved, ia, ic);
+            put(threadIdx.x, ia, ic, kx, ky, vx, vy);
+        }
+        for (int idx = threadIdx.x + blockDim.x; idx < count; idx += blockDim.x) {
+            int ia, ic;
+            size_t src;
+            new_pair(b, qo, idx, ia, ic, src);
+            const int i = idx % HALF;
+            put(idx, ia, ic, a.k_new[src + ia], a.k_new[src + ic], a.v_new[src + 2 * i], a.v_new[src + 2 * i + 1]);
         }
     };
 
@@ -386,16 +404,32 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     };
     const int first_p1 = (int)min((long long)key_end,
                                   ((long long)(key_begin >> c.log2_bs) + MAX_PIECE_BLOCKS) << c.log2_bs);
-    // The fused step's work needs the sequence's length but not its block
-    // ids: it runs while the block-table loads are in flight, before the
-    // first tile is issued (whose registers its fp64 work would compete
-    // with) and before the first piece (whose barriers also publish the new
-    // K/V rows in LDS).
-    const bool spec = c.window == 0 && b == z && spec_base < first_p1;
+    // Every load above is taken into use before the first tile goes out: a
+    // wait on one of them after that point would also wait (the counter is
+    // in order) for the tile.  The first piece's block ids go to LDS; the
+    // fused step's raw q rows go to LDS and its new-key pair and frequency
+    // are made ready; otherwise q is converted to the MFMA operands.
+    {
+        const int nblk0 = ((first_p1 - 1) >> c.log2_bs) - (key_begin >> c.log2_bs) + 1;
+#pragma unroll
+        for (int r = 0; r < MAX_PIECE_BLOCKS / 256; ++r) {
+            const int i = (int)threadIdx.x + 256 * r;
+            if (i < nblk0) sm_blk[i] = tb[r];
+        }
+    }
+    if constexpr (FUSED) {
+        fused_stage_q();
+        __asm__ volatile("" : : "v"(kx), "v"(ky), "v"(vx), "v"(vy), "v"(theta));
+    } else {
+        prepare_q();
+    }
+    const bool spec = early && spec_base < first_p1;
     if (spec) issue(spec_base, first_p1, [&](int key) { return __shfl(spec_blk, key - spec_base); });
+    // The fused step's work runs while the first tile is in flight, before
+    // the first piece (whose barriers also publish the new K/V rows in LDS).
     if constexpr (FUSED) {
         fused_angles();
-        __syncthreads();
+        __syncthreads();                    // angles, raw q rows and block ids in LDS
         fused_rotate_q();
         fused_append();
     }
@@ -406,14 +440,10 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         const int p1 = (int)min((long long)key_end, ((long long)blk0 + MAX_PIECE_BLOCKS) << c.log2_bs);
         const int nblk = ((p1 - 1) >> c.log2_bs) - blk0 + 1;
         const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
-        __syncthreads();                      // the previous piece (or the ranking) is done with LDS
-        if (p0 == key_begin) {
-            // first piece: thread i already holds block id i
-            if ((int)threadIdx.x < nblk) sm_blk[threadIdx.x] = tb;
-            for (int i = threadIdx.x + blockDim.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
-        } else {
+        __syncthreads();                      // the previous piece is done with LDS
+        // (the first piece's block ids were staged before the first tile)
+        if (p0 != key_begin)
             for (int i = threadIdx.x; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
-        }
         __syncthreads();
 
         auto staged = [&](int key) { return sm_blk[(key >> c.log2_bs) - blk0]; };
@@ -425,7 +455,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         constexpr int STRIDE = WAVES * TILE;
         int base = p0 + wave * TILE;
         if (base < p1 && !(spec && p0 == key_begin)) issue(base, p1, staged);
-        if (p0 == key_begin) prepare_q();
+        if (FUSED && p0 == key_begin) prepare_q();
         // One tile of the wave: scores, softmax, P.V, and the next tile's
         // loads.  SUBST: the tile's loaded keys may include new tokens (the
         // fused step's last tiles), whose rows are taken from LDS.
@@ -555,6 +585,14 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             }
         }
     }
+
+    // the rotated queries, when asked for (split 0 writes them): after the
+    // key loop, so that the first tile's wait does not include them
+    if (FUSED && a.q_rot && split == 0)
+        for (int idx = threadIdx.x; idx < a.rows * D; idx += blockDim.x) {
+            const int r = idx / D, d = idx - r * D, t = r / c.g;
+            if (t < nn) a.q_rot[(((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g)) * D + d] = sm_q[idx];
+        }
 }
 
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) { attn_mfma_body<false>(a); }

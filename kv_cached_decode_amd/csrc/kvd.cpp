@@ -386,13 +386,17 @@ int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, 
     Plan p;
     st = make_plan(kv, opt, &p);
     if (st != KVD_OK) return st;
-    if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && !kv->key_pos0 && !kv->q_pos) {
+    // the fused kernel appends from the block ids of one staged piece
+    const bool one_piece = (int64_t)p.split_keys + kv->block_size - 1 <=
+                           (int64_t)kvd::MFMA_PIECE_BLOCKS * kv->block_size;
+    if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && !kv->key_pos0 && !kv->q_pos && one_piece) {
         const FuseIn f{k, v, q_rot, rope_base, layout};
         return attention(kv, q, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
     }
-    // vector-ALU and prefill plans and context-parallel shards: the two
-    // kernels in a row; `out` holds the rotated queries when the caller wants none back
-    // (each output row is written only after its query row has been read)
+    // vector-ALU and prefill plans, context-parallel shards and splits of
+    // more blocks than one piece: the two kernels in a row; `out` holds the
+    // rotated queries when the caller wants none back (each output row is
+    // written only after its query row has been read)
     float* qr = q_rot ? q_rot : out;
     st = rope_append(kv, q, k, v, qr, rope_base, layout, stream);
     if (st != KVD_OK) return st;

@@ -149,5 +149,9 @@ constexpr int MFMA_WGS_PER_CU = 2;
 int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds);
 // Query rows (g*T) from which the matrix-core kernel is the default.
 constexpr int MFMA_MIN_ROWS = 2;
+// Block ids the decode matrix-core kernel stages in LDS at a time (one
+// piece of a split).  The fused step needs a split's blocks in one piece:
+// its append takes the new keys' block ids from there.
+constexpr int MFMA_PIECE_BLOCKS = 2048;
 
 }  // namespace kvd

@@ -61,6 +61,12 @@ SPECS = [workloads.small_variant(n) for n in workloads.CONFIG_ORDER[1:]] + [
                    spare_frac=0.1, seed=77),
     workloads.Spec("valu_mha_bf16", 4, 1, 8, 8, 128, 16, "bf16", (100, 3000), 10000.0, "normal",
                    "shuffled", spare_frac=0.1, seed=78),
+    # matrix-core plans with more than 256 new-key pairs per kv head (the
+    # append's later rounds): 16 tokens at g = 1, 8 tokens at g = 2
+    workloads.Spec("mha_t16", 3, 16, 8, 8, 128, 16, "bf16", (100, 900), 10000.0, "normal", "shuffled",
+                   spare_frac=0.1, seed=79),
+    workloads.Spec("g2_t8", 3, 8, 16, 8, 128, 16, "bf16", (50, 700), 500000.0, "normal_scaled",
+                   "shuffled", spare_frac=0.1, seed=80, layout=1),
 ]
 
 
@@ -201,3 +207,20 @@ def test_fused_step_replays_under_hip_graph_capture():
         step()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager)
+
+
+def test_split_longer_than_one_piece():
+    """One split of more cache blocks than the fused kernel stages at a time
+    (2048): the step runs as the two kernels in a row and stays correct."""
+    spec = workloads.Spec("one_long_split", 1, 1, 8, 2, 128, 16, "bf16", 33000, 10000.0, "normal",
+                          "shuffled", spare_frac=0.05, seed=81)
+    w = cached_workload(spec)
+    note("split longer than one piece")
+    ref_case, case = GpuCase(w), GpuCase(w)
+    n, keys, _ = kb.decode_attention_plan(case.kv, num_splits=1, kernel=kb.KVD_KERNEL_MFMA)
+    assert n == 1 and (keys + 15) // 16 > 2048
+    ref = two_calls(ref_case, kernel=kb.KVD_KERNEL_MFMA, num_splits=1)
+    got = fused(case, kernel=kb.KVD_KERNEL_MFMA, num_splits=1)
+    assert_same(ref_case, case, ref, got)
+    _, out_ref, _, _ = oracle_step(w)
+    assert_parity(spec, got[1], out_ref)
