@@ -132,6 +132,9 @@ EDGE = [
     ("verify_t8", 2, 8, 8, 4, 128, 16, "bf16", (0, 900), 0),
     ("verify_t16_f32", 1, 16, 4, 4, 64, 16, "f32", 333, 1),
     ("interleaved", 3, 1, 8, 8, 128, 64, "bf16", (1, 2000), 1),
+    # the largest chunk a step takes (T = 1024): 4096 and 1024 query rows per kv head
+    ("chunk_t1024_g4", 1, 1024, 32, 8, 128, 16, "bf16", (0, 200), 0),
+    ("chunk_t1024_mha", 2, 1024, 4, 4, 128, 64, "bf16", (10, 300), 1),
 ]
 
 
