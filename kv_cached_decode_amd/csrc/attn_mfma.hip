@@ -150,8 +150,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     const int wave = threadIdx.x >> 6;
     const int n16 = lane & 15;          // MFMA column / row-in-tile index
     const int j = lane >> 4;            // lane group
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
+    // grid (kv head, split, sequence slot): the hardware deals workgroups to
+    // the XCDs round-robin in this order, so the eight of one (slot, split)
+    // -- equal work whatever the sequence -- spread over them, instead of
+    // one split index (the first always full, the last often empty) piling
+    // onto the same XCDs
+    const int kvh = blockIdx.x;
+    const int split = blockIdx.y;
     const int z = blockIdx.z;
     const int row = n16;                // query row of this lane (rows >= M are padding)
     const bool row_ok = row < a.rows;
@@ -607,7 +612,7 @@ bool mfma_supported(int D_, int kv_bf16, int rows) { return D_ == D && kv_bf16 &
 int mfma_step_keys() { return WAVES * TILE; }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-    dim3 grid(a.num_splits, a.c.Hkv, a.c.B);
+    dim3 grid(a.c.Hkv, a.num_splits, a.c.B);
     if (a.fused)
         hipLaunchKernelGGL(decode_step_mfma_kernel, grid, dim3(256), 0, s, a);
     else

@@ -109,9 +109,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     const CacheView& c = a.c;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y % c.Hkv;
-    const int rtile = blockIdx.y / c.Hkv;
+    // grid (kv head x row tile, split, sequence): kv heads fastest, so that
+    // the round-robin dealing of workgroups to XCDs spreads equal work
+    const int kvh = blockIdx.x % c.Hkv;
+    const int rtile = blockIdx.x / c.Hkv;
+    const int split = blockIdx.y;
     const int b = blockIdx.z;
 
     const int L = c.seq_lens[b];
@@ -393,7 +395,7 @@ int valu_max_split_keys(int log2_bs) { return (VALU_MAX_STAGED_BLOCKS - 2) << lo
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s) {
     const int n_rtiles = (a.rows + a.row_tile - 1) / a.row_tile;
-    dim3 grid(a.num_splits, a.c.Hkv * n_rtiles, a.c.B);
+    dim3 grid(a.c.Hkv * n_rtiles, a.num_splits, a.c.B);
     return a.kv_bf16 ? launch_d<1>(a, grid, s) : launch_d<0>(a, grid, s);
 }
 

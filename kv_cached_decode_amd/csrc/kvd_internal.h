@@ -68,7 +68,7 @@ struct AttnArgs {
     int32_t num_splits;     // S
     int32_t split_keys;     // keys per split (multiple of the kernel's step)
     int32_t rows;           // g*T
-    int32_t row_tile;       // rows handled by one workgroup (grid.y = Hkv * row tiles)
+    int32_t row_tile;       // rows handled by one workgroup (grid.x = Hkv * row tiles)
     int32_t rank_longest;   // order work longest-first (the grid exceeds the resident slots)
     float scale_log2;       // softmax scale * log2(e)
     const float* q;         // [B][T][Hq][D]
