@@ -250,14 +250,16 @@ int32_t kvd_merge_partials(int32_t n_parts, int64_t rows, int32_t head_dim, cons
  *           as for kvd_decode_attention_ex (same workspace size).
  *
  * Results (out, q_rot, the cache) are bitwise those of the two calls in a
- * row with the same plan.  When the plan uses the matrix-core kernel and the
- * descriptor is not a context-parallel shard, one
+ * row with the same plan.  When the plan uses the matrix-core decode kernel
+ * (at most 16 query rows per kv head), the descriptor is not a
+ * context-parallel shard and a split spans at most 2048 cache blocks, one
  * kernel does all of it (plus the split combine when there are several
  * splits): each workgroup rotates its own query rows, and the workgroup whose
  * key range holds the new tokens stores their K/V rows and uses them directly.
- * Otherwise the RoPE/append kernel runs first and, if q_rot is NULL, `out`
- * holds the rotated queries in between (measured about 7% slower on a large
- * prefill chunk than with a q_rot buffer).
+ * Pass q_rot = NULL there unless the rotated queries are wanted: writing them
+ * is extra work.  Otherwise the RoPE/append kernel runs first and, if q_rot is
+ * NULL, `out` holds the rotated queries in between (measured about 7% slower
+ * on a large prefill chunk than with a q_rot buffer).
  */
 int32_t kvd_decode_step(const kvd_paged_kv *kv, const float *q, const float *k, const float *v,
                         float *q_rot, float *out, double rope_base, int32_t layout,
