@@ -115,12 +115,48 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     }
 }
 
-// Merge of context-parallel partials: one workgroup per row.  Wave 0 forms
-// the parts' weights exp(lse_p - M) (M = max_p lse_p) in LDS and their sum S,
-// so LSE = M + log S; then each thread sums its elements over the parts with
-// a nonzero weight (a part that saw no key is never read) and scales by 1/S.
-// Fixed summation order.
+// Merge of context-parallel partials: one workgroup per row.  The parts'
+// weights are exp(lse_p - M) (M = max_p lse_p), their sum S gives
+// LSE = M + log S, and each element is the weighted sum over the parts with a
+// nonzero weight (a part that saw no key is never used), scaled by 1/S.
+// Beyond eight parts, wave 0 forms the weights in LDS first.  Fixed
+// summation order.
 constexpr int MAX_PARTS = 4096;
+
+// Few parts (the usual count: one per GPU of a group): every thread loads all
+// the parts' lse and its elements of all the parts at once, one memory round
+// trip; the same weights, and parts of weight 0 are loaded but never used.
+template <int NMAX>
+__device__ inline bool merge_small(int n, int64_t rows, int D, const float* outs, const float* lses,
+                                   float* out, float* lse_out) {
+    if (n > NMAX) return false;
+    const int64_t row = blockIdx.x;
+    float l[NMAX];
+#pragma unroll
+    for (int p = 0; p < NMAX; ++p)
+        if (p < n) l[p] = lses[p * rows + row];
+    for (int d = threadIdx.x; d < D; d += COMBINE_THREADS) {
+        float x[NMAX];
+#pragma unroll
+        for (int p = 0; p < NMAX; ++p)
+            if (p < n) x[p] = outs[((size_t)p * rows + row) * D + d];
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < NMAX; ++p)
+            if (p < n) M = fmaxf(M, l[p]);
+        float S = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int p = 0; p < NMAX; ++p)
+            if (p < n) {
+                const float w = M == -INFINITY ? 0.0f : expf(l[p] - M);
+                S += w;
+                if (w > 0.0f) o += w * x[p];
+            }
+        out[(size_t)row * D + d] = o * (S > 0.0f ? 1.0f / S : 0.0f);
+        if (lse_out && d == 0) lse_out[row] = S > 0.0f ? M + logf(S) : -INFINITY;
+    }
+    return true;
+}
 
 __global__ __launch_bounds__(COMBINE_THREADS) void merge_partials_kernel(int n, int64_t rows, int D,
                                                                         const float* outs,
@@ -128,6 +164,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void merge_partials_kernel(int n, 
                                                                         float* lse_out) {
     __shared__ float sm_w[MAX_PARTS];
     __shared__ float sm_red[2];
+    if (merge_small<8>(n, rows, D, outs, lses, out, lse_out)) return;
     const int64_t row = blockIdx.x;
     if (threadIdx.x < 64) {
         float M = -INFINITY;

@@ -142,3 +142,31 @@ def test_merge_of_one_part_is_identity_and_all_empty_rows_are_zero():
     assert torch.allclose(out2.cpu(), o[0].cpu(), rtol=1e-6, atol=1e-6)
     fin = torch.isfinite(l_[0]).cpu()
     assert torch.allclose(lse2.cpu()[fin], (l_[0].cpu() + np.log(2.0))[fin], rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("P", [8, 12])
+def test_merge_of_many_parts(P):
+    """Eight parts (each thread loads every part at once) and twelve (weights
+    formed in LDS first), with rows some parts did not see (lse -inf, output
+    0) and one row no part saw: the merge formula in fp64."""
+    note("merge parts", P)
+    rng = np.random.default_rng(40 + P)
+    rows, D = 57, 128
+    o = rng.standard_normal((P, rows, D)).astype(np.float32)
+    lse = (rng.standard_normal((P, rows)) * 3.0).astype(np.float32)
+    empty = rng.random((P, rows)) < 0.25
+    empty[:, 7] = True
+    lse[empty] = -np.inf
+    o[empty] = 0.0
+    out, mlse = kb.merge_partials(torch.from_numpy(o).to(DEV), torch.from_numpy(lse).to(DEV))
+    torch.cuda.synchronize()
+    out, mlse = out.cpu().numpy(), mlse.cpu().numpy()
+    l64 = lse.astype(np.float64)
+    M = l64.max(axis=0)
+    live = np.isfinite(M)
+    w = np.where(live[None, :], np.exp(l64 - np.where(live, M, 0.0)[None, :]), 0.0)
+    S = w.sum(axis=0)
+    ref = np.einsum("pr,prd->rd", w, o.astype(np.float64)) / np.where(S > 0, S, 1.0)[:, None]
+    assert np.all(out[~live] == 0.0) and np.all(np.isneginf(mlse[~live]))
+    assert np.max(np.abs(out[live] - ref[live])) <= 1e-5 * np.max(np.abs(ref[live]))
+    assert np.max(np.abs(mlse[live] - (M + np.log(np.where(S > 0, S, 1.0)))[live])) <= 1e-5
