@@ -122,6 +122,32 @@ def timed(fn, steps, warmup):
     return start.elapsed_time(end) / steps   # ms per call
 
 
+def graph_timed_us(fn, results, calls=32, replays=20):
+    """Device time of one call of `fn` without the host's launch cost: `calls`
+    launches captured in one HIP graph, replayed `replays` times.  The graph's
+    results must equal those of an eager call (None is returned otherwise)."""
+    fn()
+    torch.cuda.synchronize()
+    eager = [r.clone() for r in results]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    for r in results:
+        r.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(r, e) for r, e in zip(results, eager)):
+        return None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (replays * calls)
+
+
 def prewarm(L, seconds=0.3):
     """Untimed: run the three call kinds in turn until the GPU's clocks have
     settled, so that the first kind timed is not the one that pays for it."""
@@ -206,6 +232,7 @@ def measure_cp_shard(steps, warmup, dev, parts=8):
     lses = torch.randn((parts,) + tuple(q.shape[:3]), dtype=torch.float32, device=dev)
     mo, ml = torch.empty_like(q), torch.empty_like(lse)
     merge_ms = timed(lambda i: kb.merge_partials(outs, lses, mo, ml), steps, warmup)
+    merge_graph_us = graph_timed_us(lambda: kb.merge_partials(outs, lses, mo, ml), (mo, ml))
     rows = s.num_seqs * s.q_tokens * s.n_q_heads
     shard_bytes = s.num_seqs * n * s.n_kv_heads * s.head_dim * 2 * 2 + rows * s.head_dim * 4 * 2 + rows * 4 \
         + s.num_seqs * (n // bs) * 4
@@ -217,6 +244,7 @@ def measure_cp_shard(steps, warmup, dev, parts=8):
             "shard_ms": round(shard_ms, 4), "shard_GBs": round(shard_bytes / (shard_ms * 1e-3) / 1e9, 1),
             "shard_frac_of_peak": round(shard_bytes / (shard_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "merge_ms": round(merge_ms, 4),
+            "merge_graph_us": None if merge_graph_us is None else round(merge_graph_us, 2),
             "exchange_bytes_per_gpu": rows * (s.head_dim + 1) * 4}
 
 
