@@ -74,14 +74,22 @@ __device__ inline s16x4 lds_tr(const char* p) {
         (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
 }
 
+// Two fp32 weights as bf16 hi + lo pairs (element 0 in the low half): hi is
+// the rounded value, lo the rounded remainder.  One conversion rounds both
+// his, and their fp32 values come back with a shift and a mask.
+__device__ inline void split_pair(float a, float b, unsigned& hi, unsigned& lo) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
+}
+
 // Reductions over lanes l, l^16, l^32, l^48 (the four lane groups holding a
 // row's keys).  permlane16_swap / permlane32_swap of a register with itself
 // leave, in every lane, its own value and its partner's (lane ^ 16, lane ^ 32)
-// in the two results, in an order that depends on the lane; max and the
-// single addition are symmetric in them, so every lane gets the same value.
-// (scores hold no NaN: a compare and select is the maximum)
-__device__ inline float max_sel(float a, float b) { return a > b ? a : b; }
-
+// in the two results, in an order that depends on the lane; the single
+// addition is symmetric in them, so every lane gets the same value.
 __device__ inline float xor_sum(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -89,11 +97,28 @@ __device__ inline float xor_sum(float x) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-__device__ inline float xor_max(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = max_sel(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return max_sel(__uint_as_float(q[0]), __uint_as_float(q[1]));
+// Maximum of two floats in one instruction.  (fmaxf on values that come out
+// of a lane exchange first quiets signalling NaNs with two more.)
+__device__ inline float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// The maxima of a and b over the four 16-lane rows at once.  permlane16_swap
+// (x, y) trades x's odd rows for y's even rows: it returns (x0 y0 x2 y2) and
+// (x1 y1 x3 y3), so the first swap and maximum leave a's and b's row pairs
+// side by side; permlane32_swap trades x's upper half for y's lower half, so
+// the second folds rows 0-1 against 2-3; the third hands each lane both
+// results.  Scores hold no NaN.
+__device__ inline void xor_max2(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const float c = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));   // rows: a01 b01 a23 b23
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+    const float e = vmax(__uint_as_float(q[0]), __uint_as_float(q[1]));   // rows: a b a b
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(e), __float_as_uint(e), false, false);
+    a = __uint_as_float(t[0]);
+    b = __uint_as_float(t[1]);
 }
 
 // A unit of work is (sequence b, row tile, split): the keys
@@ -278,13 +303,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
             }
         }
 
-    // running max m (log2 units), O^T and this lane's part of the row sums
+    // running max m (log2 units), O^T and this lane's part of the row sums.
+    // The scores accumulate onto -m (onto 0 before the row's first key), so
+    // they come out of the matrix cores relative to the running max.
+    static_assert(RB == 2, "row maxima are exchanged in pairs");
     float m[RB], lsum[RB];
-    f32x4 o[RB][8];
+    f32x4 o[RB][8], neg_m[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         m[rb] = M_EMPTY;
         lsum[rb] = 0.0f;
+        neg_m[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -303,12 +332,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                                (c.window == 0 || base >= lo_max);
             const char* kt = sm_k[buf];
             const char* vt = sm_v[buf];
-            // scores: S^T tiles (16 keys x 16 rows), keys base + 16h + 4j + i
+            // scores less the running max: S^T tiles (16 keys x 16 rows),
+            // keys base + 16h + 4j + i
             f32x4 s[RB][2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) s[rb][h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+                for (int rb = 0; rb < RB; ++rb) s[rb][h] = neg_m[rb];
                 const char* kp = kt + (16 * h + n16) * KROWB + 16 * j;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -331,43 +361,63 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                             if (key >= key_end || key > vis[rb] || key < lo[rb]) s[rb][h][i] = -INFINITY;
                         }
             }
-            // running maxima: every row moves to its maximum when one row
-            // of the wave grew past the slack
+            // running maxima: when one row of the wave saw its first key or
+            // grew past the slack, every row moves up to its tile maximum
+            // (a row without a key yet stays empty) and the tile's scores
+            // follow it
             float mx[RB];
             bool grew = false;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                float x = m[rb];
+                float x = -INFINITY;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) x = max_sel(x, s[rb][h][i]);
-                mx[rb] = xor_max(x);
-                grew |= mx[rb] > m[rb] + RESCALE_SLACK;
+                    for (int i = 0; i < 4; ++i) x = fmaxf(x, s[rb][h][i]);   // three-input maxima
+                mx[rb] = x;
             }
+            xor_max2(mx[0], mx[1]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                grew |= m[rb] == M_EMPTY ? mx[rb] > -INFINITY : mx[rb] > RESCALE_SLACK;
             if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const float alpha = fast_exp2(m[rb] - mx[rb]);
-                    m[rb] = mx[rb];
+                    const bool started = m[rb] != M_EMPTY;
+                    const float up = started ? fmaxf(mx[rb], 0.0f) : mx[rb];
+                    const float mnew = started ? m[rb] + up : (up > -INFINITY ? up : M_EMPTY);
+                    const float shift = started ? mnew - m[rb] : (mnew == M_EMPTY ? 0.0f : mnew);
+                    const float alpha = started ? fast_exp2(m[rb] - mnew) : 1.0f;
+                    m[rb] = mnew;
                     lsum[rb] *= alpha;
 #pragma unroll
                     for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= alpha;
+                    const float nm = mnew == M_EMPTY ? 0.0f : -mnew;
+                    neg_m[rb] = (f32x4){nm, nm, nm, nm};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) s[rb][h] -= shift;
                 }
             }
             bf16x8 phi[RB], plo[RB];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+            for (int rb = 0; rb < RB; ++rb) {
+                u32x4 hi, lo;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float p = fast_exp2(s[rb][h][i] - m[rb]);
-                        lsum[rb] += p;
-                        const __bf16 hi = (__bf16)p;
-                        phi[rb][4 * h + i] = hi;
-                        plo[rb][4 * h + i] = (__bf16)(p - (float)hi);
+                    for (int i = 0; i < 4; i += 2) {
+                        const float p0 = fast_exp2(s[rb][h][i]);
+                        const float p1 = fast_exp2(s[rb][h][i + 1]);
+                        lsum[rb] += p0;
+                        lsum[rb] += p1;
+                        unsigned ph, pl;
+                        split_pair(p0, p1, ph, pl);
+                        hi[2 * h + i / 2] = ph;
+                        lo[2 * h + i / 2] = pl;
                     }
+                phi[rb] = as_bf16x8(hi);
+                plo[rb] = as_bf16x8(lo);
+            }
             // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i and 16 + 4j + i
             const char* rd = vt + (4 * j + (n16 >> 2)) * VROWB + 8 * (n16 & 3);
 #pragma unroll

@@ -120,3 +120,27 @@ def test_longest_first_unit_order(splits):
     for b, n in enumerate(w.q_lens):
         assert np.all(out[b, n:] == 0.0), "padding rows must be 0"
     assert_parity(sp, out, ref)
+
+
+@pytest.mark.parametrize("big_first", [False, True])
+def test_rows_of_very_different_scales(big_first):
+    """Runs of 4 tokens (16 rows of a kv-head group at g = 4, one MFMA row
+    block) whose queries are scaled by 1 or 2e4, alternately: rows with
+    scores of a few hundredths beside rows whose scores spread over hundreds
+    (log2 units).  Each row block keeps its own running maximum while the two
+    blocks a wave holds exchange theirs together, and the large jumps of the
+    maximum rescale without overflow or loss."""
+    sp = spec("row_scales", 2, 64, 32, 8, (100, 400), 71)
+    w = workloads.make_workload(sp)
+    big = ((np.arange(sp.q_tokens) // 4) % 2 == 0) == big_first
+    f = np.where(big, 2e4, 1.0).astype(np.float32)
+    w = workloads.Workload(**{**w.__dict__, "q": (w.q * f[None, :, None, None]).astype(np.float32)})
+    note("row scales", big_first)
+    case = GpuCase(w)
+    assert kb.decode_attention_plan(case.kv)[2] == kb.KVD_KERNEL_MFMA
+    _, out = case.step()
+    _, ref, _, _ = oracle_step(w)
+    # each group of rows against its own scale (the peaky rows' outputs are
+    # single values of V; the flat rows' are averages, about 20x smaller)
+    for rows in (big, ~big):
+        assert_parity(sp, out[:, rows], ref[:, rows])
