@@ -71,7 +71,7 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *                       reads kv head h / (Hq / Hkv).
  *   head_dim            D in {16, 32, 64, 128, 256}.
  *   block_size          bs, keys per cache block: a power of two, 1..1024.
- *   num_blocks          blocks in each pool.
+ *   num_blocks          blocks in each pool; num_blocks * n_kv_heads < 2^31.
  *   max_blocks_per_seq  row stride of block_table.
  *   max_seq_len         host-side upper bound on every seq_lens[b]; it sizes
  *                       the split-K plan (no device read is needed, so a call

@@ -40,6 +40,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVES = 4;
 constexpr int D = 128;
+constexpr int LOG2_ROW_BYTES = 8;         // one cached key or value row: D bf16
+static_assert((1 << LOG2_ROW_BYTES) == D * 2, "row bytes");
 constexpr int TILE = 32;
 constexpr int RB = 2;                     // 16-row blocks per wave
 constexpr int WROWS = 16 * RB;            // query rows per wave
@@ -49,8 +51,8 @@ constexpr int VROWB = D * 2 + 32;         // LDS row stride of the V tile (trans
 constexpr int K_BYTES = TILE * KROWB;
 constexpr int V_BYTES = TILE * VROWB;
 constexpr int MAX_STAGED_BLOCKS = 4096;   // block ids of a split, staged in LDS
-constexpr int RANK_MAX = PREFILL_RANK_MAX;  // units ranked longest-first (their key counts and order share the block-id array)
-static_assert(2 * RANK_MAX <= MAX_STAGED_BLOCKS, "ranking arrays");
+constexpr int RANK_MAX = PREFILL_RANK_MAX;  // units ranked longest-first (their key counts and the units by rank share the block-id array)
+static_assert(RANK_MAX <= 256, "one unit per thread in the ranking");
 constexpr float M_EMPTY = -1e30f;
 // The running maximum of a row moves (and its sums are rescaled) only when a
 // tile's scores exceed it by more than RESCALE_SLACK (log2 units); below that
@@ -129,6 +131,8 @@ struct Unit {
     int b, rtile, split;
     int qo, n_live, key_begin, key_end, live_rows;
 };
+static_assert(RANK_MAX * (1 + sizeof(Unit) / sizeof(int)) <= MAX_STAGED_BLOCKS,
+              "ranking arrays (key counts, units by rank) share the block-id array");
 
 __device__ inline Unit unit_of(const AttnArgs& a, int u, int n_rtiles) {
     const CacheView& c = a.c;
@@ -166,40 +170,40 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     const int pos = blockIdx.x / c.Hkv;
     const int n_rtiles = (a.rows + ROWS - 1) / ROWS;
     const int n_units = a.num_splits * n_rtiles * c.B;
-    int u = pos;
+    Unit un;
     if (a.rank_longest && n_units <= RANK_MAX) {
         // Longest-first: position pos takes the unit of rank pos by key count
         // (ties by unit index; empty units last), so the longest units start
         // first and the short ones fill the slots at the end.  Every
-        // workgroup derives the same permutation.
+        // workgroup derives the same permutation; thread v describes unit v
+        // and files it under its rank.
         int* const sm_work = sm_blk;
-        int* const sm_perm = sm_blk + RANK_MAX;
+        Unit* const sm_unit = (Unit*)(sm_blk + RANK_MAX);
         const int n4 = (n_units + 3) & ~3;
-        for (int v = tid; v < n4; v += blockDim.x) {
-            int w = -1;        // padding: below every unit
-            if (v < n_units) {
-                const Unit x = unit_of(a, v, n_rtiles);
-                w = x.live_rows > 0 ? max(0, x.key_end - x.key_begin) : 0;
-            }
-            sm_work[v] = w;
+        Unit x{};
+        int w = -1;        // padding: below every unit
+        if (tid < n_units) {
+            x = unit_of(a, tid, n_rtiles);
+            w = x.live_rows > 0 ? max(0, x.key_end - x.key_begin) : 0;
         }
+        if (tid < n4) sm_work[tid] = w;
         __syncthreads();
-        for (int v = tid; v < n_units; v += blockDim.x) {
-            const int w = sm_work[v];
+        if (tid < n_units) {
             int r = 0;
             for (int i = 0; i < n4; i += 4) {
-                const int4 x = *(const int4*)(sm_work + i);
-                r += (x.x > w) + (x.y > w) + (x.z > w) + (x.w > w);
-                r += (x.x == w && i + 0 < v) + (x.y == w && i + 1 < v) + (x.z == w && i + 2 < v) +
-                     (x.w == w && i + 3 < v);
+                const int4 y = *(const int4*)(sm_work + i);
+                r += (y.x > w) + (y.y > w) + (y.z > w) + (y.w > w);
+                r += (y.x == w && i + 0 < tid) + (y.y == w && i + 1 < tid) + (y.z == w && i + 2 < tid) +
+                     (y.w == w && i + 3 < tid);
             }
-            sm_perm[r] = v;
+            sm_unit[r] = x;
         }
         __syncthreads();
-        u = sm_perm[pos];
+        un = sm_unit[pos];
         __syncthreads();       // sm_blk is reused for block ids below
+    } else {
+        un = unit_of(a, pos, n_rtiles);
     }
-    const Unit un = unit_of(a, u, n_rtiles);
     const int b = un.b, split = un.split;
     const int row0 = un.rtile * ROWS;
     const int qo = un.qo, n_live = un.n_live, live_rows = un.live_rows;
@@ -255,7 +259,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     const int blk0 = key_begin >> c.log2_bs;
     const int nblk = ((key_end - 1) >> c.log2_bs) - blk0 + 1;
     const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
-    for (int i = tid; i < nblk; i += blockDim.x) sm_blk[i] = trow[i];
+    // staged as the (block, kv head) row of the pools: blk * Hkv + kvh
+    for (int i = tid; i < nblk; i += blockDim.x) sm_blk[i] = trow[i] * c.Hkv + kvh;
     __syncthreads();
 
     // Each thread moves 2 of the 512 16-byte chunks of a K tile and 2 of the
@@ -270,10 +275,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         for (int i = 0; i < 2; ++i) {
             const int ch = tid + 256 * i;
             const int key = min(base + (ch >> 4), key_end - 1);
-            const int blk = sm_blk[(key >> c.log2_bs) - blk0];
-            const size_t slot = (((size_t)blk * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
-            kr[i] = __builtin_nontemporal_load((const u32x4*)(kbase + slot * (D * 2) + 16 * (ch & 15)));
-            vr[i] = __builtin_nontemporal_load((const u32x4*)(vbase + slot * (D * 2) + 16 * (ch & 15)));
+            const unsigned hrow = sm_blk[(key >> c.log2_bs) - blk0];
+            const size_t off = ((size_t)hrow << (c.log2_bs + LOG2_ROW_BYTES)) +
+                               ((key & bs_mask) << LOG2_ROW_BYTES | 16 * (ch & 15));
+            kr[i] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
+            vr[i] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
         }
     };
     auto stage = [&](int buf) {
@@ -307,12 +313,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     // The scores accumulate onto -m (onto 0 before the row's first key), so
     // they come out of the matrix cores relative to the running max.
     static_assert(RB == 2, "row maxima are exchanged in pairs");
-    float m[RB], lsum[RB];
+    // A row moves its maximum when a tile's relative maximum exceeds thr:
+    // the slack once it has one, -inf before its first key.
+    float m[RB], lsum[RB], thr[RB];
     f32x4 o[RB][8], neg_m[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         m[rb] = M_EMPTY;
         lsum[rb] = 0.0f;
+        thr[rb] = -INFINITY;
         neg_m[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
@@ -366,7 +375,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
             // (a row without a key yet stays empty) and the tile's scores
             // follow it
             float mx[RB];
-            bool grew = false;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 float x = -INFINITY;
@@ -377,10 +385,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                 mx[rb] = x;
             }
             xor_max2(mx[0], mx[1]);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                grew |= m[rb] == M_EMPTY ? mx[rb] > -INFINITY : mx[rb] > RESCALE_SLACK;
-            if (__builtin_amdgcn_ballot_w64(grew)) {
+            if (__builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1])) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     const bool started = m[rb] != M_EMPTY;
@@ -389,6 +394,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                     const float shift = started ? mnew - m[rb] : (mnew == M_EMPTY ? 0.0f : mnew);
                     const float alpha = started ? fast_exp2(m[rb] - mnew) : 1.0f;
                     m[rb] = mnew;
+                    thr[rb] = mnew == M_EMPTY ? -INFINITY : RESCALE_SLACK;
                     lsum[rb] *= alpha;
 #pragma unroll
                     for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= alpha;

@@ -78,6 +78,9 @@ int32_t check_desc(const kvd_paged_kv* kv) {
     if (kv->num_blocks < 1 || kv->max_blocks_per_seq < 1)
         return fail(KVD_ERR_SHAPE, "num_blocks = %d, max_blocks_per_seq = %d", kv->num_blocks,
                     kv->max_blocks_per_seq);
+    if ((int64_t)kv->num_blocks * kv->n_kv_heads > INT32_MAX)
+        return fail(KVD_ERR_UNSUPPORTED, "num_blocks * n_kv_heads = %lld (at most 2^31 - 1)",
+                    (long long)kv->num_blocks * kv->n_kv_heads);
     // a context-parallel shard may hold fewer keys than new tokens (or none),
     // and ragged chunks fewer new tokens than T
     if (kv->max_seq_len < (kv->q_pos || kv->q_lens ? 0 : kv->q_tokens_per_seq))

@@ -90,25 +90,28 @@ struct AttnArgs {
 // A split that holds no key of its sequence leaves, for its rows, a partial
 // that drops out of the merge (running max -1e30, sum 0, output 0), so the
 // merge combines every split without reading the sequence lengths.  With a
-// single split (only a context-parallel shard can hold no key of a
-// sequence) the rows are final: output 0, lse -inf.
+// single split (a context-parallel shard without a key of the sequence, or
+// rows of padding tokens past a ragged chunk) the rows are final: output 0,
+// lse -inf.
 __device__ inline void write_empty_partials(const AttnArgs& a, int b, int kvh, int split, int row0,
                                             int nrows) {
     const CacheView& c = a.c;
     const int D = c.D;
-    for (int idx = threadIdx.x; idx < nrows * (D + 2); idx += blockDim.x) {
-        const int r = row0 + idx / (D + 2), e = idx % (D + 2);
-        if (r >= a.rows) continue;
+    const int lq = __builtin_ctz(D) - 2;      // D / 4 float4s a row (D a power of two >= 16)
+    const int n4 = (min(row0 + nrows, a.rows) - row0) << lq;
+    const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int idx = threadIdx.x; idx < n4; idx += blockDim.x) {
+        const int r = row0 + (idx >> lq), e4 = idx & ((1 << lq) - 1);
         const int t = r / c.g;
         const size_t qrow = ((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g);
         if (a.num_splits == 1) {
-            if (e < D) a.out[qrow * D + e] = 0.0f;
-            else if (e == D && a.lse) a.lse[qrow] = -INFINITY;
-            continue;
+            *(float4*)(a.out + qrow * D + 4 * e4) = zero;
+            if (e4 == 0 && a.lse) a.lse[qrow] = -INFINITY;
+        } else {
+            const size_t part = qrow * a.num_splits + split;
+            *(float4*)(a.part_o + part * D + 4 * e4) = zero;
+            if (e4 == 0) *(float2*)(a.part_ml + part * 2) = make_float2(-1e30f, 0.0f);
         }
-        const size_t part = qrow * a.num_splits + split;
-        if (e < D) a.part_o[part * D + e] = 0.0f;
-        else a.part_ml[part * 2 + (e - D)] = e == D ? -1e30f : 0.0f;
     }
 }
 
