@@ -62,6 +62,7 @@ BAD = [
     (dict(block_size=24), kb.KVD_ERR_UNSUPPORTED),
     (dict(block_size=2048), kb.KVD_ERR_UNSUPPORTED),
     (dict(num_blocks=0), kb.KVD_ERR_SHAPE),
+    (dict(num_blocks=2 ** 30, n_q_heads=8, n_kv_heads=2), kb.KVD_ERR_UNSUPPORTED),   # 2^31 pool rows
     (dict(max_seq_len=0), kb.KVD_ERR_SHAPE),
     (dict(q_tokens_per_seq=4, max_seq_len=3), kb.KVD_ERR_SHAPE),
     (dict(q_lens=FAKE + 0x60001), kb.KVD_ERR_SHAPE),         # misaligned chunk lengths
