@@ -121,6 +121,24 @@ __device__ inline int lpt_rank_pick(int B, int z, const int* sm_len, int* sm_pic
     return *sm_pick;
 }
 
+// The same ranking for batches of at most 64 sequences inside one wave: lane
+// b holds sequence b's length packed with its index into a distinct key
+// (longer first, then lower index; lengths past 2^26 - 1 compare as equal,
+// which only changes the order), each lane counts the keys above its own
+// through lane reads, and the lane of rank z names the sequence.  Every wave
+// ranks on its own: no LDS and no barrier.  Returns the sequence and, in
+// len, its length.
+__device__ inline int lpt_rank_pick_wave(int B, int z, const int* seq_lens, int& len) {
+    const int lane = threadIdx.x & 63;
+    const int L = lane < B ? seq_lens[lane] : 0;
+    const unsigned key = lane < B ? (unsigned)min(max(L, 0), (1 << 26) - 1) << 6 | (63 - lane) : 0u;
+    int rank = 0;
+    for (int i = 0; i < B; ++i) rank += __builtin_amdgcn_readlane(key, i) > key;
+    const int pick = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < B && rank == z));
+    len = __builtin_amdgcn_readlane(L, pick);
+    return pick;
+}
+
 template <bool FUSED>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // the V tiles during the key loop, then the per-wave outputs
@@ -242,7 +260,9 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     }
     int b = z;
     int L = c.seq_lens[z];
-    if (ranked) {
+    if (ranked && c.B <= 64) {
+        b = lpt_rank_pick_wave(c.B, z, c.seq_lens, L);
+    } else if (ranked) {
         // the ranking borrows the V-tile LDS (unused until the key loop)
         int* sm_len = (int*)sm_v;
         for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];
