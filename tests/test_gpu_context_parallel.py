@@ -88,9 +88,21 @@ CASES = [("llama3_8b", 3, 0, kb.KVD_KERNEL_MFMA), ("mtp_verify", 3, 0, kb.KVD_KE
 @pytest.mark.parametrize("name,P,window,kernel", CASES,
                          ids=[f"{n}-P{p}-w{w}-k{k}" for n, p, w, k in CASES])
 def test_shards_merge_to_whole_cache(name, P, window, kernel):
-    spec = workloads.small_variant(name)
+    check_shards(workloads.small_variant(name), P, window, kernel)
+
+
+@pytest.mark.parametrize("window", [0, 64])
+def test_prefill_shards_merge_to_whole_cache(window):
+    """A chunk of 40 new tokens per sequence (160 query rows per kv head: the
+    prefill kernel) cut into 3 shards, the same checks."""
+    spec = workloads.Spec("cp_prefill", 3, 40, 32, 8, 128, 16, "bf16", (100, 500), 10000.0, "normal",
+                          "shuffled", spare_frac=0.1, seed=83)
+    check_shards(spec, 3, window, kb.KVD_KERNEL_AUTO)
+
+
+def check_shards(spec, P, window, kernel):
     w = cached_workload(spec)
-    note("context parallel", name, P, window, kernel)
+    note("context parallel", spec.name, P, window, kernel)
     case = GpuCase(w, window=window)
     cuts = shard_cuts(w, P, seed=P + window)
     q_rot, outs, lses, merged, mlse, shards = run_shards(case, cuts, kernel, window)
