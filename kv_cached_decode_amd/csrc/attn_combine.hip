@@ -16,11 +16,11 @@
 namespace kvd {
 namespace {
 
-// One workgroup of COMBINE_THREADS per query row.  Up to 8 splits, each
-// thread reads everything it needs in one go; beyond that the split weights
-// 2^(m_s - M) / sum are formed once in LDS (lanes over splits, wave
-// reductions), then each thread sums its splits with independent loads in
-// flight.
+// Up to eight splits (the common case), each thread reads everything it
+// needs in one go; beyond that, one workgroup of COMBINE_THREADS per query
+// row forms the split weights 2^(m_s - M) / sum once in LDS (lanes over
+// splits, wave reductions), then each thread sums its splits with
+// independent loads in flight.
 constexpr int COMBINE_THREADS = 128;
 constexpr int MAX_STAGED_SPLITS = 1024;
 
@@ -36,41 +36,50 @@ __device__ inline float wave_sum(float x) {
     return x;
 }
 
-// Few splits (the common case): every thread loads its own elements and all
-// (m, l) pairs at once, so the kernel costs one memory round trip.
-template <int NMAX>
-__device__ inline bool combine_small(const AttnArgs& a, size_t qrow, int n) {
-    if (n > NMAX) return false;
+// Up to eight splits: D/4 threads a row, one float4 of it each, and as many
+// rows as fill 256 threads in one workgroup (the same arithmetic as above,
+// element by element).
+constexpr int ROWS_THREADS = 256;
+constexpr int ROWS_MAX_SPLITS = 8;
+
+__global__ __launch_bounds__(ROWS_THREADS) void attn_combine_rows_kernel(AttnArgs a) {
     const CacheView& c = a.c;
-    const int S = a.num_splits;
-    const float* ml = a.part_ml + qrow * S * 2;
-    const float* po = a.part_o + qrow * S * c.D;
-    for (int d = threadIdx.x; d < c.D; d += COMBINE_THREADS) {
-        float m[NMAX], l[NMAX], o[NMAX];
+    const int lq = __builtin_ctz(c.D) - 2;                 // threads a row: D / 4
+    const int rpw = ROWS_THREADS >> lq;                    // rows a workgroup
+    const size_t rows = (size_t)c.B * c.T * c.Hq;
+    const size_t qrow = (size_t)blockIdx.x * rpw + (threadIdx.x >> lq);
+    const int e4 = threadIdx.x & ((1 << lq) - 1);
+    if (qrow >= rows) return;
+    const int n = a.num_splits;
+    const float2* ml = (const float2*)(a.part_ml + qrow * n * 2);
+    const float4* po = (const float4*)(a.part_o + qrow * n * c.D) + e4;
+    float2 w[ROWS_MAX_SPLITS];
+    float4 o[ROWS_MAX_SPLITS];
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if (s < n) {
-                m[s] = ml[2 * s];
-                l[s] = ml[2 * s + 1];
-                o[s] = po[(size_t)s * c.D + d];
-            }
+    for (int s = 0; s < ROWS_MAX_SPLITS; ++s)
+        if (s < n) {
+            w[s] = ml[s];
+            o[s] = po[(size_t)s * (c.D >> 2)];
         }
-        float M = -INFINITY;
+    float M = -INFINITY;
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if (s < n) M = fmaxf(M, m[s]);
-        float Ls = 0.0f, O = 0.0f;
+    for (int s = 0; s < ROWS_MAX_SPLITS; ++s)
+        if (s < n) M = fmaxf(M, w[s].x);
+    float Ls = 0.0f;
+    float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if (s < n) {
-                const float w = exp2f(m[s] - M);
-                Ls += l[s] * w;
-                O += o[s] * w;
-            }
-        a.out[qrow * c.D + d] = finish_out(O, Ls);
-        if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
-    }
-    return true;
+    for (int s = 0; s < ROWS_MAX_SPLITS; ++s)
+        if (s < n) {
+            const float f = exp2f(w[s].x - M);
+            Ls += w[s].y * f;
+            O.x += o[s].x * f;
+            O.y += o[s].y * f;
+            O.z += o[s].z * f;
+            O.w += o[s].w * f;
+        }
+    *(float4*)(a.out + qrow * c.D + 4 * e4) =
+        make_float4(finish_out(O.x, Ls), finish_out(O.y, Ls), finish_out(O.z, Ls), finish_out(O.w, Ls));
+    if (a.lse && e4 == 0) a.lse[qrow] = finish_lse(M, Ls);
 }
 
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs a) {
@@ -80,7 +89,6 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     const size_t qrow = blockIdx.x;                     // (b*T + t)*Hq + h
     const int S = a.num_splits;
     const int n = S;
-    if (combine_small<8>(a, qrow, n)) return;
     const float* ml = a.part_ml + qrow * S * 2;
     const float* po = a.part_o + qrow * S * c.D;
 
@@ -206,7 +214,13 @@ hipError_t launch_merge_partials(int n_parts, int64_t rows, int D, const float* 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
     const size_t rows = (size_t)a.c.B * a.c.T * a.c.Hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(COMBINE_THREADS), 0, s, a);
+    if (a.num_splits <= ROWS_MAX_SPLITS) {
+        const size_t rpw = ROWS_THREADS / (a.c.D / 4);
+        hipLaunchKernelGGL(attn_combine_rows_kernel, dim3((unsigned)((rows + rpw - 1) / rpw)),
+                           dim3(ROWS_THREADS), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(COMBINE_THREADS), 0, s, a);
+    }
     return hipGetLastError();
 }
 

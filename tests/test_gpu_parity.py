@@ -116,6 +116,22 @@ def test_split_count_does_not_change_the_result(splits):
     assert rel_err(out, out_auto) < 1e-5
 
 
+@needs_gpu
+@pytest.mark.parametrize("D,dtype", [(16, "f32"), (32, "bf16"), (64, "f32"), (256, "bf16")])
+def test_split_merge_every_head_dim(D, dtype):
+    """Three splits merged at every head dim (the merge lays D/4 threads on a
+    row, 256/(D/4) rows a workgroup, the last one partly filled)."""
+    spec = workloads.Spec(f"splits_d{D}", 3, 2, 8, 2, D, 16, dtype, (100, 900), 10000.0, "normal",
+                          "shuffled", spare_frac=0.1, seed=D)
+    w = cached_workload(spec)
+    note("split merge", D, dtype)
+    case = GpuCase(w)
+    q_rot = kb.rope_append_kv(case.kv, case.q, case.k, case.v, rope_base=spec.rope_base)
+    out = case.attention(q_rot, num_splits=3)
+    _, out_ref, _, _ = oracle_step(w)
+    assert_parity(spec, out, out_ref)
+
+
 EDGE = [
     # name, B, T, Hq, Hkv, D, bs, dtype, ctx, layout
     ("single_key", 3, 1, 8, 2, 128, 16, "bf16", 0, 0),
