@@ -9,10 +9,11 @@
 // pos * theta_i (theta_i = base^(-2i/D) from the host) are evaluated in fp64
 // once per workgroup and shared through LDS; every head's pair is then
 // rotated in fp64 and rounded once: to fp32 for q_rot and an fp32 cache, to
-// bf16 (round to nearest even) for a bf16 cache.  The volume is tiny
-// (B*T*(Hq + 2*Hkv)*D elements), so the kernel is latency-bound: a thread
-// handles one rotation pair of a few heads, with all its loads issued first.
-// Padding tokens of ragged chunks do nothing.
+// bf16 (round to nearest even) for a bf16 cache.  A decode step moves little
+// (B*T*(Hq + 2*Hkv)*D elements) and is latency-bound; a prefill chunk moves
+// tens of MB, so a thread takes four pairs of a head with two 16-byte loads
+// and stores, all its loads issued first.  Padding tokens of ragged chunks do
+// nothing.
 #include "bf16_round.h"
 #include "kvd_internal.h"
 #include "rope_math.h"
@@ -20,14 +21,53 @@
 namespace kvd {
 namespace {
 
-// Heads of one token are numbered q heads, then k heads, then v heads.  A
-// workgroup takes HEADS_PER_SLOT * (256 / (D/2)) of them: thread (slot, i)
-// handles pair i of heads slot, slot + slots, ... (four heads), so a token's
-// angles are evaluated by few workgroups and every thread's loads and stores
-// are in flight together.
-constexpr int HEADS_PER_SLOT = 4;
+// A thread takes four rotation pairs of a head: pairs 4k .. 4k+3, whose
+// elements are the float4s at 4k and D/2 + 4k (pairs (i, i + D/2)) or at 8k
+// and 8k + 4 (pairs (2i, 2i+1)); D/8 threads cover a head, 256/(D/8) heads
+// a round.  Heads of one token are numbered q heads, then k heads, then v
+// heads (v is only rounded, through the same element split).  A workgroup
+// takes `rounds` rounds of heads of one token, every load issued before the
+// token's angles are formed; the host picks the rounds so that a batch of
+// few tokens still spreads over many workgroups.
+constexpr int MAX_ROUNDS = 4;
 
-__global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
+struct Quad {
+    float4 a, b;     // the two float4s of the thread's pairs
+};
+
+__device__ inline float pick(const float4& v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+__device__ inline void put(float4& v, int j, float x) {
+    if (j == 0) v.x = x; else if (j == 1) v.y = x; else if (j == 2) v.z = x; else v.w = x;
+}
+
+// pair j of the thread (0..3): its two elements within the quad
+__device__ inline void pair_get(const Quad& q, int interleaved, int j, float& x, float& y) {
+    if (interleaved) {
+        const float4& v = j < 2 ? q.a : q.b;
+        x = pick(v, 2 * (j & 1));
+        y = pick(v, 2 * (j & 1) + 1);
+    } else {
+        x = pick(q.a, j);
+        y = pick(q.b, j);
+    }
+}
+__device__ inline void pair_set(Quad& q, int interleaved, int j, float x, float y) {
+    if (interleaved) {
+        float4& v = j < 2 ? q.a : q.b;
+        put(v, 2 * (j & 1), x);
+        put(v, 2 * (j & 1) + 1, y);
+    } else {
+        put(q.a, j, x);
+        put(q.b, j, y);
+    }
+}
+
+__device__ inline uint2 bf16x4_from_f32(const float4& v) {
+    return make_uint2((uint32_t)bf16_from_f32(v.x) | (uint32_t)bf16_from_f32(v.y) << 16,
+                      (uint32_t)bf16_from_f32(v.z) | (uint32_t)bf16_from_f32(v.w) << 16);
+}
+
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a, int rounds) {
     __shared__ double cs[128];
     __shared__ double sn[128];
     const CacheView& c = a.c;
@@ -35,36 +75,28 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const int b = token / c.T, t = token - b * c.T;
     if (t >= n_new(c, b)) return;      // a padding token of a ragged chunk: nothing to rotate or store
     const int D = c.D, half = D >> 1;
-    const int slots = blockDim.x / half;
-    const int slot = (int)threadIdx.x / half;
-    const int i = (int)threadIdx.x % half;
+    const int lt = __builtin_ctz(D) - 3;            // threads a head: D / 8
+    const int slots = 256 >> lt;
+    const int slot = (int)threadIdx.x >> lt;
+    const int k = (int)threadIdx.x & ((1 << lt) - 1);
     const int heads = c.Hq + 2 * c.Hkv;
-    int ia, ic;
-    rope_pair(i, half, a.interleaved, ia, ic);
+    const int offa = a.interleaved ? 8 * k : 4 * k;
+    const int offb = a.interleaved ? 8 * k + 4 : half + 4 * k;
+    const int h0 = blockIdx.y * rounds * slots + slot;
 
     // This thread's inputs first (they do not depend on the angles), so their
     // latency overlaps the fp64 angle evaluation below.
-    float x0[HEADS_PER_SLOT], x1[HEADS_PER_SLOT];
-    int head[HEADS_PER_SLOT];
+    Quad x[MAX_ROUNDS];
 #pragma unroll
-    for (int r = 0; r < HEADS_PER_SLOT; ++r) {
-        head[r] = (blockIdx.y * HEADS_PER_SLOT + r) * slots + slot;
-        x0[r] = x1[r] = 0.0f;
-        const int hd = head[r];
-        if (slot >= slots || hd >= heads) continue;
-        if (hd < c.Hq) {
-            const size_t o = ((size_t)token * c.Hq + hd) * D;
-            x0[r] = a.q[o + ia];
-            x1[r] = a.q[o + ic];
-        } else if (hd < c.Hq + c.Hkv) {
-            const size_t o = ((size_t)token * c.Hkv + (hd - c.Hq)) * D;
-            x0[r] = a.k[o + ia];
-            x1[r] = a.k[o + ic];
-        } else {
-            const size_t o = ((size_t)token * c.Hkv + (hd - c.Hq - c.Hkv)) * D + 2 * i;
-            x0[r] = a.v[o];
-            x1[r] = a.v[o + 1];
-        }
+    for (int r = 0; r < MAX_ROUNDS; ++r) {
+        x[r].a = x[r].b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const int hd = h0 + r * slots;
+        if (r >= rounds || hd >= heads) continue;
+        const float* src = hd < c.Hq ? a.q + ((size_t)token * c.Hq + hd) * D
+                         : hd < c.Hq + c.Hkv ? a.k + ((size_t)token * c.Hkv + (hd - c.Hq)) * D
+                                             : a.v + ((size_t)token * c.Hkv + (hd - c.Hq - c.Hkv)) * D;
+        x[r].a = *(const float4*)(src + offa);
+        x[r].b = *(const float4*)(src + offb);
     }
     // the token's local slot, and its global position for the rotation (they
     // differ in a context-parallel shard)
@@ -75,47 +107,57 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     for (int p = threadIdx.x; p < half; p += blockDim.x)
         rope_angle(kernarg_double(offsetof(RopeAppendArgs, theta), p), pos, cs[p], sn[p]);
     __syncthreads();
-    if (slot >= slots) return;
 
     const int off = local & ((1 << c.log2_bs) - 1);   // the cache slot of this token
 #pragma unroll
-    for (int r = 0; r < HEADS_PER_SLOT; ++r) {
-        const int hd = head[r];
-        if (hd >= heads) break;
+    for (int r = 0; r < MAX_ROUNDS; ++r) {
+        const int hd = h0 + r * slots;
+        if (r >= rounds || hd >= heads) break;
+        Quad y = x[r];
+        if (hd < c.Hq + c.Hkv) {
+            // q or k: every pair turned in fp64, rounded once
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x0, x1;
+                pair_get(x[r], a.interleaved, j, x0, x1);
+                double xr, yr;
+                rope_rotate(x0, x1, cs[4 * k + j], sn[4 * k + j], xr, yr);
+                if (hd < c.Hq || !a.kv_bf16) {
+                    pair_set(y, a.interleaved, j, (float)xr, (float)yr);
+                } else {
+                    // bf16 keys round straight from fp64: keep the bits in the floats' places
+                    pair_set(y, a.interleaved, j, __uint_as_float(bf16_from_f64(xr)),
+                             __uint_as_float(bf16_from_f64(yr)));
+                }
+            }
+        }
         if (hd < c.Hq) {
-            // query -> q_rot (fp32); q and q_rot may alias: the pair is read
-            // and written by this thread only.
-            const size_t o = ((size_t)token * c.Hq + hd) * D;
-            double xr, yr;
-            rope_rotate(x0[r], x1[r], cs[i], sn[i], xr, yr);
-            a.q_rot[o + ia] = (float)xr;
-            a.q_rot[o + ic] = (float)yr;
-        } else if (hd < c.Hq + c.Hkv) {
-            const int h = hd - c.Hq;
-            const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
-            double xr, yr;
-            rope_rotate(x0[r], x1[r], cs[i], sn[i], xr, yr);
-            if (a.kv_bf16) {
-                uint16_t* kc = (uint16_t*)c.k;
-                kc[dst + ia] = bf16_from_f64(xr);
-                kc[dst + ic] = bf16_from_f64(yr);
+            // query -> q_rot (fp32); q and q_rot may alias: the elements are
+            // read and written by this thread only
+            float* dst = a.q_rot + ((size_t)token * c.Hq + hd) * D;
+            *(float4*)(dst + offa) = y.a;
+            *(float4*)(dst + offb) = y.b;
+            continue;
+        }
+        const bool is_k = hd < c.Hq + c.Hkv;
+        const int h = is_k ? hd - c.Hq : hd - c.Hq - c.Hkv;
+        const size_t row = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;
+        if (a.kv_bf16) {
+            uint16_t* dst = (uint16_t*)(is_k ? c.k : c.v) + row;
+            if (is_k) {
+                // the rounded bits sit in the low halves of the floats
+                *(uint2*)(dst + offa) = make_uint2(__float_as_uint(y.a.x) | __float_as_uint(y.a.y) << 16,
+                                                   __float_as_uint(y.a.z) | __float_as_uint(y.a.w) << 16);
+                *(uint2*)(dst + offb) = make_uint2(__float_as_uint(y.b.x) | __float_as_uint(y.b.y) << 16,
+                                                   __float_as_uint(y.b.z) | __float_as_uint(y.b.w) << 16);
             } else {
-                float* kc = (float*)c.k;
-                kc[dst + ia] = (float)xr;
-                kc[dst + ic] = (float)yr;
+                *(uint2*)(dst + offa) = bf16x4_from_f32(y.a);
+                *(uint2*)(dst + offb) = bf16x4_from_f32(y.b);
             }
         } else {
-            const int h = hd - c.Hq - c.Hkv;
-            const size_t dst = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D + 2 * i;
-            if (a.kv_bf16) {
-                uint16_t* vc = (uint16_t*)c.v;
-                vc[dst] = bf16_from_f32(x0[r]);
-                vc[dst + 1] = bf16_from_f32(x1[r]);
-            } else {
-                float* vc = (float*)c.v;
-                vc[dst] = x0[r];
-                vc[dst + 1] = x1[r];
-            }
+            float* dst = (float*)(is_k ? c.k : c.v) + row;
+            *(float4*)(dst + offa) = y.a;
+            *(float4*)(dst + offb) = y.b;
         }
     }
 }
@@ -125,11 +167,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
     const int tokens = a.c.B * a.c.T;
     if (tokens == 0) return hipSuccess;
-    const int half = a.c.D / 2;
-    const int heads_per_wg = HEADS_PER_SLOT * (256 / half);
+    const int slots = 256 / (a.c.D / 8);
     const int heads = a.c.Hq + 2 * a.c.Hkv;
-    dim3 grid(tokens, (heads + heads_per_wg - 1) / heads_per_wg);
-    hipLaunchKernelGGL(rope_append_kernel, grid, dim3(256), 0, s, a);
+    const int total = (heads + slots - 1) / slots;            // rounds of heads a token
+    // few tokens: one round a workgroup (more workgroups); many: up to
+    // MAX_ROUNDS, so that every workgroup keeps more loads in flight
+    const int rounds = tokens >= 512 ? (total < MAX_ROUNDS ? total : MAX_ROUNDS) : 1;
+    dim3 grid(tokens, (total + rounds - 1) / rounds);
+    hipLaunchKernelGGL(rope_append_kernel, grid, dim3(256), 0, s, a, rounds);
     return hipGetLastError();
 }
 
