@@ -139,6 +139,49 @@ __device__ inline int lpt_rank_pick_wave(int B, int z, const int* seq_lens, int&
     return pick;
 }
 
+// Unit order, when the batch has several splits: the units are (sequence,
+// split) pairs, and a split of a short sequence can hold as many keys as a
+// split of a long one, so the units themselves are ranked.  Thread v (one
+// per unit, up to 256) forms unit v = (v / S, v % S)'s key count exactly as
+// the workgroup that runs it will, packs it with the unit index into a
+// distinct key (more keys first, then lower index), files the unit under its
+// rank and its sequence length beside it; grid position pos (split index
+// fastest, then sequence slot) takes the unit of rank pos.  Returns the unit
+// and, in len, its sequence's length.
+__device__ inline int lpt_unit_pick(const AttnArgs& a, int pos, unsigned* sm_key, int* sm_unit,
+                                    int* sm_len, int& len) {
+    const CacheView& c = a.c;
+    const int S = a.num_splits;
+    const int n = c.B * S, n4 = (n + 3) & ~3;
+    const int v = threadIdx.x;
+    unsigned key = 0u;                  // padding: below every unit
+    int L = 0;
+    if (v < n) {
+        const int bb = v / S, s = v - bb * S;
+        L = c.seq_lens[bb];
+        const int qo = q_local0(c, bb, L);
+        const int k0 = range_start(c, qo) + s * a.split_keys;
+        const int keys = max(0, min(range_end(c, L, qo, n_new(c, bb)), k0 + a.split_keys) - k0);
+        key = ((unsigned)min(keys, (1 << 23) - 1) << 8 | (unsigned)(255 - v)) + 1u;
+    }
+    if (v < n4) sm_key[v] = key;
+    __syncthreads();
+    if (v < n) {
+        int r = 0;
+        for (int i = 0; i < n4; i += 4) {
+            const uint4 y = *(const uint4*)(sm_key + i);
+            r += (y.x > key) + (y.y > key) + (y.z > key) + (y.w > key);
+        }
+        sm_unit[r] = v;
+        sm_len[r] = L;
+    }
+    __syncthreads();
+    const int u = sm_unit[pos];
+    len = sm_len[pos];
+    __syncthreads();                    // the ranking's LDS is reused next
+    return u;
+}
+
 template <bool FUSED>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // the V tiles during the key loop, then the per-wave outputs
@@ -174,7 +217,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // one split index (the first always full, the last often empty) piling
     // onto the same XCDs
     const int kvh = blockIdx.x;
-    const int split = blockIdx.y;
+    int split = blockIdx.y;
     const int z = blockIdx.z;
     const int row = n16;                // query row of this lane (rows >= M are padding)
     const bool row_ok = row < a.rows;
@@ -260,7 +303,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     }
     int b = z;
     int L = c.seq_lens[z];
-    if (ranked && c.B <= 64) {
+    if (ranked && a.num_splits > 1 && c.B * a.num_splits <= 256) {
+        // the ranking borrows the V-tile LDS (unused until the key loop)
+        const int u = lpt_unit_pick(a, split + a.num_splits * z, (unsigned*)sm_v, (int*)sm_v + 256,
+                                    (int*)sm_v + 512, L);
+        b = u / a.num_splits;
+        split = u - b * a.num_splits;
+    } else if (ranked && c.B <= 64) {
         b = lpt_rank_pick_wave(c.B, z, c.seq_lens, L);
     } else if (ranked) {
         // the ranking borrows the V-tile LDS (unused until the key loop)
