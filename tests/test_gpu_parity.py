@@ -132,6 +132,28 @@ def test_split_merge_every_head_dim(D, dtype):
     assert_parity(spec, out, out_ref)
 
 
+@needs_gpu
+@pytest.mark.parametrize("D,dtype,layout,Hq,Hkv", [(128, "bf16", 1, 32, 8), (64, "f32", 1, 64, 8),
+                                                  (16, "bf16", 0, 8, 2), (256, "f32", 0, 16, 4)])
+def test_rope_append_many_tokens(D, dtype, layout, Hq, Hkv):
+    """RoPE + append of 600 tokens (several head rounds a workgroup) in both
+    pairings and every head dim: the pools bit for bit and q_rot within one
+    fp32 rounding of the oracle."""
+    spec = workloads.Spec(f"rope_many_d{D}", 3, 200, Hq, Hkv, D, 16, dtype, (0, 300), 500000.0, "normal",
+                          "shuffled", spare_frac=0.1, seed=D + layout, layout=layout)
+    w = cached_workload(spec)
+    note("rope many tokens", D, dtype, layout)
+    case = GpuCase(w)
+    q_rot = kb.rope_append_kv(case.kv, case.q, case.k, case.v, rope_base=spec.rope_base, layout=layout)
+    torch.cuda.synchronize()
+    kp, vp = case.pools()
+    oc = oracle_cache(w)
+    q_ref = oc.rope_append_kv(w.q, w.k, w.v, spec.rope_base, layout)
+    assert np.array_equal(kp.view(np.uint8), oc.k_pool.view(np.uint8)), "K pool differs"
+    assert np.array_equal(vp.view(np.uint8), oc.v_pool.view(np.uint8)), "V pool differs"
+    assert_qrot(q_rot.cpu().numpy(), q_ref)
+
+
 EDGE = [
     # name, B, T, Hq, Hkv, D, bs, dtype, ctx, layout
     ("single_key", 3, 1, 8, 2, 128, 16, "bf16", 0, 0),
