@@ -28,12 +28,15 @@
 // part and write the empty result.  Split ranges, windows, ragged chunks and
 // context-parallel shards follow the same rules as the decode kernels
 // (kvd_internal.h).
+#include <type_traits>
+
 #include "kvd_internal.h"
 
 namespace kvd {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -86,6 +89,23 @@ __device__ inline void split_pair(float a, float b, unsigned& hi, unsigned& lo) 
     const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
     lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
 }
+
+// Two fp32 values as an fp16 pair (element 0 in the low half), rounded to
+// nearest even.
+__device__ inline unsigned f16_pair(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
+// A bf16 pair as an fp16 pair: exact for magnitudes in [2^-14, 65504].
+__device__ inline unsigned f16_from_bf16_pair(unsigned u) {
+    return f16_pair(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+
+// The fast pass's weights in fp16 are scaled by this power of two (they stay
+// at most 2^RESCALE_SLACK = 2^8 before it, so at most 2^15 after).
+constexpr float P_SCALE = 128.0f;
 
 // Reductions over lanes l, l^16, l^32, l^48 (the four lane groups holding a
 // row's keys).  permlane16_swap / permlane32_swap of a register with itself
@@ -173,6 +193,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char sm_k[2][K_BYTES];
     __shared__ __attribute__((aligned(16))) char sm_v[2][V_BYTES];
     __shared__ __attribute__((aligned(16))) int sm_blk[MAX_STAGED_BLOCKS];
+    __shared__ int sm_v_normal, sm_nonfinite;   // the fast pass's verdict
 
     const CacheView& c = a.c;
     const int tid = threadIdx.x;
@@ -277,6 +298,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
     // staged as the (block, kv head) row of the pools: blk * Hkv + kvh
     for (int i = tid; i < nblk; i += blockDim.x) sm_blk[i] = trow[i] * c.Hkv + kvh;
+    if (tid == 0) {
+        sm_v_normal = 0;
+        sm_nonfinite = 0;
+    }
     __syncthreads();
 
     // Each thread moves 2 of the 512 16-byte chunks of a K tile and 2 of the
@@ -296,14 +321,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                                ((key & bs_mask) << LOG2_ROW_BYTES | 16 * (ch & 15));
             kr[i] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
             vr[i] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
-        }
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ch = tid + 256 * i;
-            *(u32x4*)(sm_k[buf] + (ch >> 4) * KROWB + 16 * (ch & 15)) = kr[i];
-            *(u32x4*)(sm_v[buf] + (ch >> 4) * VROWB + 16 * (ch & 15)) = vr[i];
         }
     };
     load(key_begin);
@@ -333,131 +350,191 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     // the slack once it has one, -inf before its first key.
     float m[RB], lsum[RB], thr[RB];
     f32x4 o[RB][8], neg_m[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m[rb] = M_EMPTY;
-        lsum[rb] = 0.0f;
-        thr[rb] = -INFINITY;
-        neg_m[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    }
 
-    stage(0);
-    __syncthreads();
-    if (key_begin + TILE < key_end) load(key_begin + TILE);
-
-    int buf = 0;
-    for (int base = key_begin; base < key_end; base += TILE, buf ^= 1) {
-        // wave-uniform: does any live row of the wave see a key of the tile,
-        // and does every one see all of them?
-        const bool active = wave_live && base <= vis_last && (c.window == 0 || base + TILE - 1 >= lo_min);
-        if (active) {
-            const bool whole = base + TILE <= key_end && base + TILE - 1 <= vis_first &&
-                               (c.window == 0 || base >= lo_max);
-            const char* kt = sm_k[buf];
-            const char* vt = sm_v[buf];
-            // scores less the running max: S^T tiles (16 keys x 16 rows),
-            // keys base + 16h + 4j + i
-            f32x4 s[RB][2];
+    // The key loop.  The fast pass (F16) feeds P.V to the matrix cores in
+    // fp16, one MFMA where bf16 hi + lo takes two: V converted as it is
+    // staged (exact for magnitudes in [2^-14, 65504]), the weights scaled by
+    // P_SCALE (fp16 keeps 11 significant bits; weights below 2^-31 of a row's
+    // maximum flush to zero, at most 6e-5 of the sum over 2^17 keys).  It
+    // hands the unit to the exact pass -- bf16 V, weights as bf16 hi + lo --
+    // when a V element lay beyond fp16's range (a result comes out
+    // non-finite) or none lay in its normal range (they would keep a few
+    // bits), and returns whether it stands.
+    auto run = [&](auto f16_tag) -> bool {
+        constexpr bool F16 = decltype(f16_tag)::value;
+        unsigned vexp = 0u;             // the staged fp16 exponent fields, ORed
+        auto stage = [&](int buf, bool f16) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int i = 0; i < 2; ++i) {
+                const int ch = tid + 256 * i;
+                *(u32x4*)(sm_k[buf] + (ch >> 4) * KROWB + 16 * (ch & 15)) = kr[i];
+                u32x4 vs = vr[i];
+                if (f16) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) s[rb][h] = neg_m[rb];
-                const char* kp = kt + (16 * h + n16) * KROWB + 16 * j;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 kop = as_bf16x8(*(const u32x4*)(kp + 64 * kk));
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        s[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[rb][kk], s[rb][h], 0, 0, 0);
-                        s[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[rb][kk], s[rb][h], 0, 0, 0);
+                    for (int q = 0; q < 4; ++q) {
+                        vs[q] = f16_from_bf16_pair(vs[q]);
+                        vexp |= vs[q] & 0x7c007c00u;
                     }
                 }
+                *(u32x4*)(sm_v[buf] + (ch >> 4) * VROWB + 16 * (ch & 15)) = vs;
             }
-            if (!whole) {
+        };
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            m[rb] = M_EMPTY;
+            lsum[rb] = 0.0f;
+            thr[rb] = -INFINITY;
+            neg_m[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+
+        stage(0, F16);
+        __syncthreads();
+        if (key_begin + TILE < key_end) load(key_begin + TILE);
+
+        int buf = 0;
+        for (int base = key_begin; base < key_end; base += TILE, buf ^= 1) {
+            // wave-uniform: does any live row of the wave see a key of the tile,
+            // and does every one see all of them?
+            const bool active = wave_live && base <= vis_last && (c.window == 0 || base + TILE - 1 >= lo_min);
+            if (active) {
+                const bool whole = base + TILE <= key_end && base + TILE - 1 <= vis_first &&
+                                   (c.window == 0 || base >= lo_max);
+                const char* kt = sm_k[buf];
+                const char* vt = sm_v[buf];
+                // scores less the running max: S^T tiles (16 keys x 16 rows),
+                // keys base + 16h + 4j + i
+                f32x4 s[RB][2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) s[rb][h] = neg_m[rb];
+                    const char* kp = kt + (16 * h + n16) * KROWB + 16 * j;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const bf16x8 kop = as_bf16x8(*(const u32x4*)(kp + 64 * kk));
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            s[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[rb][kk], s[rb][h], 0, 0, 0);
+                            s[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[rb][kk], s[rb][h], 0, 0, 0);
+                        }
+                    }
+                }
+                if (!whole) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = base + 16 * h + 4 * j + i;
+                                if (key >= key_end || key > vis[rb] || key < lo[rb]) s[rb][h][i] = -INFINITY;
+                            }
+                }
+                // running maxima: when one row of the wave saw its first key or
+                // grew past the slack, every row moves up to its tile maximum
+                // (a row without a key yet stays empty) and the tile's scores
+                // follow it
+                float mx[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float x = -INFINITY;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[rb][h][i]);   // three-input maxima
+                    mx[rb] = x;
+                }
+                xor_max2(mx[0], mx[1]);
+                if (__builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1])) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const bool started = m[rb] != M_EMPTY;
+                        const float up = started ? fmaxf(mx[rb], 0.0f) : mx[rb];
+                        const float mnew = started ? m[rb] + up : (up > -INFINITY ? up : M_EMPTY);
+                        const float shift = started ? mnew - m[rb] : (mnew == M_EMPTY ? 0.0f : mnew);
+                        const float alpha = started ? fast_exp2(m[rb] - mnew) : 1.0f;
+                        m[rb] = mnew;
+                        thr[rb] = mnew == M_EMPTY ? -INFINITY : RESCALE_SLACK;
+                        lsum[rb] *= alpha;
+#pragma unroll
+                        for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= alpha;
+                        const float nm = mnew == M_EMPTY ? 0.0f : -mnew;
+                        neg_m[rb] = (f32x4){nm, nm, nm, nm};
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) s[rb][h] -= shift;
+                    }
+                }
+                u32x4 phi[RB], plo[RB];      // fp16 weights (F16), or bf16 hi and lo
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int key = base + 16 * h + 4 * j + i;
-                            if (key >= key_end || key > vis[rb] || key < lo[rb]) s[rb][h][i] = -INFINITY;
+                        for (int i = 0; i < 4; i += 2) {
+                            const float p0 = fast_exp2(s[rb][h][i]);
+                            const float p1 = fast_exp2(s[rb][h][i + 1]);
+                            lsum[rb] += p0;
+                            lsum[rb] += p1;
+                            if constexpr (F16) {
+                                phi[rb][2 * h + i / 2] = f16_pair(p0 * P_SCALE, p1 * P_SCALE);
+                            } else {
+                                unsigned ph, pl;
+                                split_pair(p0, p1, ph, pl);
+                                phi[rb][2 * h + i / 2] = ph;
+                                plo[rb][2 * h + i / 2] = pl;
+                            }
                         }
-            }
-            // running maxima: when one row of the wave saw its first key or
-            // grew past the slack, every row moves up to its tile maximum
-            // (a row without a key yet stays empty) and the tile's scores
-            // follow it
-            float mx[RB];
+                // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i and 16 + 4j + i
+                const char* rd = vt + (4 * j + (n16 >> 2)) * VROWB + 8 * (n16 & 3);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                float x = -INFINITY;
+                for (int nt = 0; nt < 8; ++nt) {
+                    const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * VROWB + 32 * nt));
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x = fmaxf(x, s[rb][h][i]);   // three-input maxima
-                mx[rb] = x;
-            }
-            xor_max2(mx[0], mx[1]);
-            if (__builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1])) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const bool started = m[rb] != M_EMPTY;
-                    const float up = started ? fmaxf(mx[rb], 0.0f) : mx[rb];
-                    const float mnew = started ? m[rb] + up : (up > -INFINITY ? up : M_EMPTY);
-                    const float shift = started ? mnew - m[rb] : (mnew == M_EMPTY ? 0.0f : mnew);
-                    const float alpha = started ? fast_exp2(m[rb] - mnew) : 1.0f;
-                    m[rb] = mnew;
-                    thr[rb] = mnew == M_EMPTY ? -INFINITY : RESCALE_SLACK;
-                    lsum[rb] *= alpha;
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= alpha;
-                    const float nm = mnew == M_EMPTY ? 0.0f : -mnew;
-                    neg_m[rb] = (f32x4){nm, nm, nm, nm};
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) s[rb][h] -= shift;
-                }
-            }
-            bf16x8 phi[RB], plo[RB];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                u32x4 hi, lo;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const float p0 = fast_exp2(s[rb][h][i]);
-                        const float p1 = fast_exp2(s[rb][h][i + 1]);
-                        lsum[rb] += p0;
-                        lsum[rb] += p1;
-                        unsigned ph, pl;
-                        split_pair(p0, p1, ph, pl);
-                        hi[2 * h + i / 2] = ph;
-                        lo[2 * h + i / 2] = pl;
+                    for (int rb = 0; rb < RB; ++rb) {
+                        if constexpr (F16) {
+                            o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(f16x8, vop), __builtin_bit_cast(f16x8, phi[rb]), o[rb][nt], 0, 0, 0);
+                        } else {
+                            o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, as_bf16x8(phi[rb]), o[rb][nt], 0, 0, 0);
+                            o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, as_bf16x8(plo[rb]), o[rb][nt], 0, 0, 0);
+                        }
                     }
-                phi[rb] = as_bf16x8(hi);
-                plo[rb] = as_bf16x8(lo);
-            }
-            // O^T += V^T . P^T; lane (n16, j) reads V rows 4j + i and 16 + 4j + i
-            const char* rd = vt + (4 * j + (n16 >> 2)) * VROWB + 8 * (n16 & 3);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 vop = join(lds_tr(rd + 32 * nt), lds_tr(rd + 16 * VROWB + 32 * nt));
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[rb], o[rb][nt], 0, 0, 0);
-                    o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[rb], o[rb][nt], 0, 0, 0);
                 }
-            }
 
+            }
+            // the next tile into the other buffer (read two tiles ago, released
+            // by the last barrier), then the one after it from HBM
+            if (base + TILE < key_end) stage(buf ^ 1, F16);
+            __syncthreads();
+            if (base + 2 * TILE < key_end) load(base + 2 * TILE);
         }
-        // the next tile into the other buffer (read two tiles ago, released
-        // by the last barrier), then the one after it from HBM
-        if (base + TILE < key_end) stage(buf ^ 1);
-        __syncthreads();
-        if (base + 2 * TILE < key_end) load(base + 2 * TILE);
+        if constexpr (F16) {
+            bool finite = __builtin_isfinite(lsum[0]) && __builtin_isfinite(lsum[1]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(o[rb][nt][i]);
+            if (vexp != 0u) sm_v_normal = 1;
+            if (!finite) sm_nonfinite = 1;
+            __syncthreads();
+            if (sm_nonfinite || !sm_v_normal) {    // the same in every lane
+                __syncthreads();                    // (keeps the two passes apart for the compiler)
+                return false;
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= 1.0f / P_SCALE;
+        }
+        return true;
+    };
+    if (!run(std::true_type{})) {
+        load(key_begin);
+        run(std::false_type{});
     }
 
     // row n16's sum over the four lane groups; O^T element (dim 16nt + 4j + i, row n16)

@@ -144,3 +144,33 @@ def test_rows_of_very_different_scales(big_first):
     # single values of V; the flat rows' are averages, about 20x smaller)
     for rows in (big, ~big):
         assert_parity(sp, out[:, rows], ref[:, rows])
+
+
+def _scale_v(w, factor, keys_every=1):
+    """The workload with V scaled by a power of two (exact in bf16 and fp32):
+    the cached rows of every keys_every-th slot of the pool, and the new
+    tokens' rows."""
+    bits = w.v_pool.astype(np.uint32) << 16
+    f = bits.view(np.float32).copy()
+    sl = f[:, :, ::keys_every, :]
+    sl *= np.float32(factor)
+    v_pool = (f.view(np.uint32) >> 16).astype(np.uint16)
+    v_pool[np.isnan(f)] = w.v_pool[np.isnan(f)]          # poisoned slots stay as they were
+    return workloads.Workload(**{**w.__dict__, "v_pool": v_pool, "v": (w.v * np.float32(factor)).astype(np.float32)})
+
+
+@pytest.mark.parametrize("factor,every", [(2.0 ** 18, 5), (2.0 ** -20, 1)], ids=["beyond_fp16", "below_fp16"])
+def test_v_outside_fp16_range(factor, every):
+    """V rows beyond fp16's range (2^18 x N(0,1)/sqrt(128) on every fifth
+    slot) or all below its normal range (2^-20 x): the units that meet them
+    are recomputed with bf16 weights and V, and every row matches the oracle."""
+    sp = spec("v_range", 2, 64, 32, 8, (100, 400), 72)
+    w = _scale_v(workloads.make_workload(sp), factor, every)
+    note("v outside fp16", factor, every)
+    case = GpuCase(w)
+    assert kb.decode_attention_plan(case.kv)[2] == kb.KVD_KERNEL_MFMA
+    _, out = case.step()
+    kp, vp = case.pools()
+    _, ref, kp_ref, vp_ref = oracle_step(w)
+    assert np.array_equal(vp, vp_ref)
+    assert_parity(sp, out, ref)
