@@ -18,8 +18,8 @@
 // barrier per tile).  Per wave, row block and tile, as in the decode kernel:
 //   S^T[32 keys x 16 rows] = K . Q^T   (K from LDS, Q as bf16 hi + lo),
 //   online softmax per row (the row sits in lane l%16),
-//   O^T[128 x 16 rows] += V^T . P^T    (V^T read transposed from LDS, P as
-//   bf16 hi + lo).
+//   O^T[128 x 16 rows] += V^T . P^T    (V^T read transposed from LDS; V and
+//   P in fp16, or bf16 V with P as bf16 hi + lo when V leaves fp16's range).
 // The loop ends at the last key any row of the tile sees.  A wave skips the
 // tiles none of its rows sees (past the causal end of its last row, before
 // the window of its first), and leaves out the mask on tiles every one of its
