@@ -201,9 +201,10 @@ int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options
  * seq_lens (tail slots, unused blocks) are never read, whatever they hold.
  * For a fixed plan the result is bitwise deterministic (no atomics).
  *
- * Arithmetic.  fp32 caches: fp32 throughout (within about 1e-5 of the fp64
- * definition).  bf16 caches: products on the matrix cores with fp32
- * accumulation; q enters as a bf16 hi + lo pair (about 16 significant bits),
+ * Arithmetic.  fp32 caches, and bf16 caches on the vector-ALU kernel: fp32
+ * vector arithmetic on the cached values.  bf16 caches on the matrix cores
+ * (head_dim 128, two or more query rows per kv head): fp32 accumulation; q
+ * enters as a bf16 hi + lo pair (about 16 significant bits),
  * the softmax weights likewise for up to 16 query rows per kv head (normwise
  * error near 1e-6); with more rows P.V runs in fp16 (normwise error near
  * 1e-4), and a (sequence, row tile, split) unit whose V leaves fp16's range
