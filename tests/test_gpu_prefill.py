@@ -159,17 +159,18 @@ def _scale_v(w, factor, keys_every=1):
     return workloads.Workload(**{**w.__dict__, "v_pool": v_pool, "v": (w.v * np.float32(factor)).astype(np.float32)})
 
 
+@pytest.mark.parametrize("splits", [0, 3])
 @pytest.mark.parametrize("factor,every", [(2.0 ** 18, 5), (2.0 ** -20, 1)], ids=["beyond_fp16", "below_fp16"])
-def test_v_outside_fp16_range(factor, every):
+def test_v_outside_fp16_range(factor, every, splits):
     """V rows beyond fp16's range (2^18 x N(0,1)/sqrt(128) on every fifth
     slot) or all below its normal range (2^-20 x): the units that meet them
     are recomputed with bf16 weights and V, and every row matches the oracle."""
     sp = spec("v_range", 2, 64, 32, 8, (100, 400), 72)
     w = _scale_v(workloads.make_workload(sp), factor, every)
-    note("v outside fp16", factor, every)
+    note("v outside fp16", factor, every, splits)
     case = GpuCase(w)
-    assert kb.decode_attention_plan(case.kv)[2] == kb.KVD_KERNEL_MFMA
-    _, out = case.step()
+    assert kb.decode_attention_plan(case.kv, num_splits=splits)[2] == kb.KVD_KERNEL_MFMA
+    _, out = case.step(num_splits=splits)
     kp, vp = case.pools()
     _, ref, kp_ref, vp_ref = oracle_step(w)
     assert np.array_equal(vp, vp_ref)
