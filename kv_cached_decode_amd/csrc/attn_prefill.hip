@@ -103,9 +103,12 @@ __device__ inline unsigned f16_from_bf16_pair(unsigned u) {
     return f16_pair(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
 
-// The fast pass's weights in fp16 are scaled by this power of two (they stay
-// at most 2^RESCALE_SLACK = 2^8 before it, so at most 2^15 after).
-constexpr float P_SCALE = 128.0f;
+// The fast pass's weights in fp16 are scaled by 2^P_SCALE_LOG2 (they stay at
+// most 2^RESCALE_SLACK = 2^8 before it, so at most 2^15 after).  The scale
+// rides in the scores: they accumulate onto P_SCALE_LOG2 - m, so exp2 yields
+// the scaled weights, O and the row sums carry the same factor, and the
+// maximum less P_SCALE_LOG2 is what the unit exports.
+constexpr float P_SCALE_LOG2 = 7.0f;
 
 // Reductions over lanes l, l^16, l^32, l^48 (the four lane groups holding a
 // row's keys).  permlane16_swap / permlane32_swap of a register with itself
@@ -343,18 +346,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         }
 
     // running max m (log2 units), O^T and this lane's part of the row sums.
-    // The scores accumulate onto -m (onto 0 before the row's first key), so
-    // they come out of the matrix cores relative to the running max.
+    // The scores accumulate onto off - m (onto off before the row's first
+    // key; off = P_SCALE_LOG2 on the fast pass, else 0), so they come out of
+    // the matrix cores relative to the running max, offset by off.
     static_assert(RB == 2, "row maxima are exchanged in pairs");
     // A row moves its maximum when a tile's relative maximum exceeds thr:
-    // the slack once it has one, -inf before its first key.
+    // the slack (plus off) once it has one, -inf before its first key.
     float m[RB], lsum[RB], thr[RB];
     f32x4 o[RB][8], neg_m[RB];
 
     // The key loop.  The fast pass (F16) feeds P.V to the matrix cores in
     // fp16, one MFMA where bf16 hi + lo takes two: V converted as it is
     // staged (exact for magnitudes in [2^-14, 65504]), the weights scaled by
-    // P_SCALE (fp16 keeps 11 significant bits; weights below 2^-31 of a row's
+    // 2^P_SCALE_LOG2 (fp16 keeps 11 significant bits; weights below 2^-31 of a row's
     // maximum flush to zero, at most 6e-5 of the sum over 2^17 keys).  It
     // hands the unit to the exact pass -- bf16 V, weights as bf16 hi + lo --
     // when a V element lay beyond fp16's range (a result comes out
@@ -362,7 +366,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     // bits), and returns whether it stands.
     auto run = [&](auto f16_tag) -> bool {
         constexpr bool F16 = decltype(f16_tag)::value;
-        unsigned vexp = 0u;             // the staged fp16 exponent fields, ORed
+        constexpr float off = F16 ? P_SCALE_LOG2 : 0.0f;
+        unsigned vexp = 0u;             // the staged fp16 pairs, ORed (their exponent fields tell)
         auto stage = [&](int buf, bool f16) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         vs[q] = f16_from_bf16_pair(vs[q]);
-                        vexp |= vs[q] & 0x7c007c00u;
+                        vexp |= vs[q];
                     }
                 }
                 *(u32x4*)(sm_v[buf] + (ch >> 4) * VROWB + 16 * (ch & 15)) = vs;
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
             m[rb] = M_EMPTY;
             lsum[rb] = 0.0f;
             thr[rb] = -INFINITY;
-            neg_m[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            neg_m[rb] = (f32x4){off, off, off, off};
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) o[rb][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
         }
@@ -451,16 +456,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         const bool started = m[rb] != M_EMPTY;
-                        const float up = started ? fmaxf(mx[rb], 0.0f) : mx[rb];
+                        const float mxr = mx[rb] - off;          // the tile's maximum less m
+                        const float up = started ? fmaxf(mxr, 0.0f) : mxr;
                         const float mnew = started ? m[rb] + up : (up > -INFINITY ? up : M_EMPTY);
                         const float shift = started ? mnew - m[rb] : (mnew == M_EMPTY ? 0.0f : mnew);
                         const float alpha = started ? fast_exp2(m[rb] - mnew) : 1.0f;
                         m[rb] = mnew;
-                        thr[rb] = mnew == M_EMPTY ? -INFINITY : RESCALE_SLACK;
+                        thr[rb] = mnew == M_EMPTY ? -INFINITY : RESCALE_SLACK + off;
                         lsum[rb] *= alpha;
 #pragma unroll
                         for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= alpha;
-                        const float nm = mnew == M_EMPTY ? 0.0f : -mnew;
+                        const float nm = (mnew == M_EMPTY ? 0.0f : -mnew) + off;
                         neg_m[rb] = (f32x4){nm, nm, nm, nm};
 #pragma unroll
                         for (int h = 0; h < 2; ++h) s[rb][h] -= shift;
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                             lsum[rb] += p0;
                             lsum[rb] += p1;
                             if constexpr (F16) {
-                                phi[rb][2 * h + i / 2] = f16_pair(p0 * P_SCALE, p1 * P_SCALE);
+                                phi[rb][2 * h + i / 2] = f16_pair(p0, p1);
                             } else {
                                 unsigned ph, pl;
                                 split_pair(p0, p1, ph, pl);
@@ -518,17 +524,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                 for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(o[rb][nt][i]);
-            if (vexp != 0u) sm_v_normal = 1;
+            if ((vexp & 0x7c007c00u) != 0u) sm_v_normal = 1;
             if (!finite) sm_nonfinite = 1;
             __syncthreads();
             if (sm_nonfinite || !sm_v_normal) {    // the same in every lane
                 __syncthreads();                    // (keeps the two passes apart for the compiler)
                 return false;
             }
+            // O and the row sums both carry 2^off: the output stands, and the
+            // maximum takes the factor out of the exported (m, l)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt) o[rb][nt] *= 1.0f / P_SCALE;
+                if (m[rb] != M_EMPTY) m[rb] -= off;
         }
         return true;
     };
