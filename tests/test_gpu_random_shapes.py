@@ -33,7 +33,7 @@ def random_case(i):
     return spec, window
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(48))
 def test_random_shape(i):
     spec, window = random_case(i)
     w = workloads.make_workload(spec)
