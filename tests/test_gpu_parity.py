@@ -173,6 +173,12 @@ EDGE = [
     # the largest chunk a step takes (T = 1024): 4096 and 1024 query rows per kv head
     ("chunk_t1024_g4", 1, 1024, 32, 8, 128, 16, "bf16", (0, 200), 0),
     ("chunk_t1024_mha", 2, 1024, 4, 4, 128, 64, "bf16", (10, 300), 1),
+    # large blocks through each kernel: matrix-core decode with splits, the
+    # prefill kernel (block ids staged per split), the vector-ALU kernel
+    ("decode_bs_128", 4, 1, 32, 8, 128, 128, "bf16", (1000, 9000), 0),
+    ("prefill_bs_256", 2, 40, 8, 2, 128, 256, "bf16", (100, 2500), 0),
+    ("prefill_bs_1024", 1, 24, 16, 4, 128, 1024, "bf16", (2000, 5000), 1),
+    ("valu_bs_512_f32", 2, 1, 8, 2, 128, 512, "f32", (100, 3000), 1),
 ]
 
 
