@@ -7,22 +7,31 @@ kvd_decode_step, which does RoPE at each token's position, the paged append
 and split-K decode attention (one fused kernel on matrix-core plans, plus the
 split combine).  The same work as two calls (kvd_rope_append_kv, then
 kvd_decode_attention) and the attention call alone are timed beside it.
-The headline workload is the Llama-3-8B-shaped layer (batch 16, 32 q / 8 kv
-heads, head_dim 128, context 4096, bf16 cache).  Inputs are seeded synthetic
-tensors already resident in HBM.  Successive steps rotate over several
-layers' caches (distinct buffers) so that no step finds its cache in the
-256 MB Infinity Cache left behind by the previous one.
+
+The headline workload is the long-context layer (batch 4, 64 q / 8 kv heads,
+head_dim 128, context 131072, paged bf16 cache with block 64), the largest
+configuration of the five; the others are reported under their own names.
+Inputs are seeded synthetic tensors already resident in HBM.  Successive
+steps rotate over several layers' caches (distinct buffers, at least 1 GiB in
+all) so that no step finds its cache in the 256 MB Infinity Cache left behind
+by the previous one.
 
 Rank 0 prints ONE JSON line.  `value` is tokens/s of the whole step (B*T new
-tokens per step).  `roofline` is for the step call (the fused kernel and the
-combine): algorithmic bytes per call / its average duration measured with HIP
-events on the launch stream.  `cpu_baseline` times the fp64 oracle on the
-host cores on a bounded sample of the same workload.
+tokens per step) over exactly K timed steps; `roofline` is for the step call
+(the fused kernel and the combine): algorithmic bytes per call / its average
+duration over those K steps, measured with HIP events on the launch stream.
+Every workload (the headline included) is also timed as the median of 20
+repetitions of 20 back-to-back calls, and as the median of 20 replays of a
+HIP graph holding 20 calls; each is reported as a fraction of the 8 TB/s peak
+and of a plain streaming-read kernel's rate on the same device.
+`cpu_baseline` times the fp64 oracle on the host cores on a bounded sample of
+the headline workload; every other workload carries its own oracle rate.
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -37,7 +46,8 @@ from kv_cached_decode_amd import workloads  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-HEADLINE = "llama3_8b"
+HEADLINE = "long_ctx"
+REPS, CALLS = 20, 20
 KERNEL_SOURCES = ["kvd.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_prefill.hip", "attn_combine.hip",
                   "rope_append.hip", "kvd_internal.h", "bf16_round.h", "rope_math.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -55,6 +65,34 @@ def to_dev_pool(pool, dev):
     if pool.dtype == np.uint16:
         return torch.from_numpy(pool.view(np.int16)).to(dev).view(torch.bfloat16)
     return torch.from_numpy(pool).to(dev)
+
+
+def describe_data(spec):
+    """The input recipe of a workload, in words."""
+    dist = {"uniform0.1": "U[-0.1, 0.1]", "normal": "N(0,1)", "normal_scaled": "N(0,1)/sqrt(128)"}[spec.dist]
+    parts = [f"seeded {dist} values", f"{spec.kv_dtype} cache"]
+    if isinstance(spec.ctx, tuple):
+        parts.append(f"ragged contexts U{{{spec.ctx[0]}..{spec.ctx[1]}}}")
+    if spec.chunk:
+        parts.append(f"ragged chunks U{{{spec.chunk[0]}..{spec.chunk[1]}}} new tokens")
+    if spec.big_keys:
+        parts.append(f"{spec.big_keys} keys per sequence scaled by {spec.big_key_factor:g}")
+    table = {"inorder": "in-order paged table", "shuffled": "shuffled paged table",
+             "single": "contiguous cache (one block per sequence)"}[spec.table]
+    parts.append(f"{table}, block {spec.block_size}")
+    if spec.spare_frac:
+        parts.append(f"{spec.spare_frac:.0%} spare blocks and every tail slot NaN/Inf-poisoned")
+    if spec.prefix:
+        parts.append("cache built by appends of raw prefix tokens")
+    return "synthetic (" + "; ".join(parts) + ")"
+
+
+def workload_text(w):
+    s = w.spec
+    ctx = f"context {s.ctx[0]}..{s.ctx[1]}" if isinstance(s.ctx, tuple) else f"context {s.ctx}"
+    t = f"T={s.q_tokens}" + (f" (chunks {s.chunk[0]}..{s.chunk[1]})" if s.chunk else "")
+    return (f"{s.name}: decode step of one attention layer, B={s.num_seqs} {t} Hq={s.n_q_heads} "
+            f"Hkv={s.n_kv_heads} D={s.head_dim} {ctx} bs={s.block_size} {s.kv_dtype}")
 
 
 class Layers:
@@ -110,6 +148,9 @@ class Layers:
 
 
 def timed(fn, steps, warmup):
+    """The contract's timing: `warmup` untimed calls, then exactly `steps`
+    calls bracketed by synchronisation and timed with HIP events on the
+    launch stream.  Returns ms per call."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -119,33 +160,64 @@ def timed(fn, steps, warmup):
         fn(i)
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps   # ms per call
+    return start.elapsed_time(end) / steps
 
 
-def graph_timed_us(fn, results, calls=32, replays=20):
-    """Device time of one call of `fn` without the host's launch cost: `calls`
-    launches captured in one HIP graph, replayed `replays` times.  The graph's
-    results must equal those of an eager call (None is returned otherwise)."""
-    fn()
+def reps_timed(fn, reps=REPS, calls=CALLS):
+    """`reps` repetitions of `calls` back-to-back calls, each repetition
+    between its own pair of HIP events.  Returns the median ms per call and
+    the spread (min, max) over the repetitions."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    i = 0
+    ev[0].record()
+    for r in range(reps):
+        for _ in range(calls):
+            fn(i)
+            i += 1
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[r].elapsed_time(ev[r + 1]) / calls for r in range(reps)]
+    return statistics.median(per), (min(per), max(per))
+
+
+def graph_timed(fn, results, calls=CALLS, replays=REPS):
+    """Device time per call without the host's launch cost: calls 0..calls-1
+    of `fn` captured in one HIP graph, replayed `replays` times, each replay
+    between its own HIP events; the median ms per call.  The graph's results
+    must equal those of the same calls made eagerly (None otherwise)."""
+    for i in range(calls):
+        fn(i)
     torch.cuda.synchronize()
     eager = [r.clone() for r in results]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(calls):
-            fn()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(calls):
+            fn(i)
+    torch.cuda.synchronize()
     for r in results:
         r.fill_(float("nan"))
     g.replay()
     torch.cuda.synchronize()
     if not all(torch.equal(r, e) for r, e in zip(results, eager)):
         return None
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(replays):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for r in range(replays):
         g.replay()
-    end.record()
+        ev[r + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e3 / (replays * calls)
+    per = [ev[r].elapsed_time(ev[r + 1]) / calls for r in range(replays)]
+    del g
+    return statistics.median(per)
+
+
+def graph_timed_us(fn, results, calls=32, replays=20):
+    """graph_timed for a call that takes no index, in microseconds."""
+    ms = graph_timed(lambda i: fn(), results, calls, replays)
+    return None if ms is None else ms * 1e3
 
 
 def prewarm(L, seconds=0.3):
@@ -167,29 +239,100 @@ def layers_for(w):
     return int(min(8, max(1, -(-(1 << 30) // kv_bytes))))
 
 
-def measure(name, steps, warmup, dev, kernel=0, num_splits=0):
+def stream_probe(dev, nbytes=2 << 30):
+    """The plain streaming-read kernel (kvd_probe_stream_read) over a 2 GiB
+    buffer at several grid shapes: the median GB/s of 20 timed reads each.
+    Returns the best shape's figure and the whole sweep."""
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sweep = []
+    for wgs in (256, 512, 1024, 2048):
+        for threads in (256, 512, 1024):
+            for unroll in (4, 16):
+                fn = lambda i: kb.probe_stream_read(buf, wgs, threads, unroll, sink)  # noqa: E731
+                for i in range(3):
+                    fn(i)
+                ms, _ = reps_timed(fn, reps=20, calls=1)
+                sweep.append({"workgroups": wgs, "threads": threads, "unroll": unroll,
+                              "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    del buf
+    torch.cuda.empty_cache()
+    best = max(sweep, key=lambda r: r["GBs"])
+    one_per_cu = max((r for r in sweep if r["workgroups"] == 256), key=lambda r: r["GBs"])
+    return {"GBs": best["GBs"], "frac_of_peak": round(best["GBs"] / PEAK_HBM_GBS, 4),
+            "best_shape": {k: best[k] for k in ("workgroups", "threads", "unroll")},
+            "GBs_256_workgroups": one_per_cu["GBs"], "bytes_read": nbytes, "sweep": sweep}
+
+
+def oracle_rate(w, budget_s=3.0):
+    """The fp64 oracle (as it stands) on the host cores for this workload:
+    RoPE + append of every new token, then attention over a seeded sample of
+    query rows that grows until it takes about budget_s (every row if that
+    is sooner).  Returns query tokens/s, counting a row's share of its token."""
+    import oracle
+    s = w.spec
+    dt = oracle.ORACLE_BF16 if s.kv_dtype == "bf16" else oracle.ORACLE_F32
+    oc = oracle.OracleCache(num_seqs=s.num_seqs, q_tokens=s.q_tokens, n_q_heads=s.n_q_heads,
+                            n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, block_size=s.block_size,
+                            k_pool=w.k_pool.copy(), v_pool=w.v_pool.copy(), block_table=w.block_table,
+                            seq_lens=w.seq_lens, cache_dtype=dt, q_lens=w.q_lens)
+    t0 = time.perf_counter()
+    q_rot = oc.rope_append_kv(w.q, w.k, w.v, s.rope_base, s.layout)
+    t_rope = time.perf_counter() - t0
+    total = s.num_seqs * s.q_tokens * s.n_q_heads
+    rng = np.random.default_rng(0)
+    n = max(1, total // 64)
+    while True:
+        rows = np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
+        t1 = time.perf_counter()
+        oc.decode_attention_rows(q_rot, rows)
+        t_attn = time.perf_counter() - t1
+        if t_attn >= budget_s / 2 or rows.size == total:
+            break
+        n *= 4
+    real_tokens = int(w.q_lens.sum()) if w.q_lens is not None else s.num_seqs * s.q_tokens
+    # time of a whole step at this rate: RoPE/append as measured, attention
+    # scaled from the sample to every row
+    t_step = t_rope + t_attn * total / rows.size
+    return {"tokens_per_s": round(real_tokens / t_step, 2), "cores": oracle.threads(),
+            "sample": f"RoPE+append of all {real_tokens} new tokens ({t_rope:.2f} s), attention of "
+                      f"{rows.size} of {total} query rows ({t_attn:.2f} s), scaled to the whole step"}
+
+
+def measure(name, steps, warmup, dev, kernel=0, num_splits=0, reps=REPS, graph=True, contract=False,
+            oracle_budget=3.0):
+    """Time one workload.  With `contract`, the step is first timed over
+    exactly `steps` calls after `warmup` (the headline's figures)."""
     w = workloads.make_workload(workloads.CONFIGS[name])
     n_layers = layers_for(w)
     L = Layers(w, n_layers, dev, kernel, num_splits)
     s = w.spec
     prewarm(L)
-    step_ms = timed(L.step, steps, warmup)
-    two_ms = timed(L.two_calls, steps, warmup)
-    attn_ms = timed(L.attention, steps, warmup)
+    res = {"workload": workload_text(w), "data": describe_data(s), "layers_rotated": n_layers,
+           "plan": {"splits": L.plan[0], "keys_per_split": L.plan[1],
+                    "kernel": ["auto", "valu", "mfma"][L.plan[2]]}}
+    if contract:
+        res["contract_step_ms"] = timed(L.step, steps, warmup)
+    step_ms, step_spread = reps_timed(L.step, reps)
+    two_ms, _ = reps_timed(L.two_calls, reps)
+    attn_ms, _ = reps_timed(L.attention, reps)
+    graph_ms = graph_timed(L.step, [L.out]) if graph else None
     nb = w.algorithmic_bytes()
     tokens = int(w.q_lens.sum()) if w.q_lens is not None else s.num_seqs * s.q_tokens
-    res = {
-        "workload": name, "layers_rotated": n_layers, "plan": {"splits": L.plan[0], "keys_per_split": L.plan[1],
-                                                               "kernel": ["auto", "valu", "mfma"][L.plan[2]]},
-        "step_ms": step_ms, "two_call_step_ms": two_ms, "attn_ms": attn_ms,
+    res.update({
+        "step_ms": step_ms, "step_ms_spread": list(step_spread), "graph_step_ms": graph_ms,
+        "two_call_step_ms": two_ms, "attn_ms": attn_ms,
         "tokens_per_s": tokens / (step_ms * 1e-3),
         "attn_tokens_per_s": tokens / (attn_ms * 1e-3),
         "attn_bytes": nb["attention"], "step_bytes": nb["step"],
         "attn_GBs": nb["attention"] / (attn_ms * 1e-3) / 1e9,
         "step_GBs": nb["step"] / (step_ms * 1e-3) / 1e9,
-    }
+    })
     res["attn_frac_of_peak"] = res["attn_GBs"] / PEAK_HBM_GBS
     res["step_frac_of_peak"] = res["step_GBs"] / PEAK_HBM_GBS
+    if graph_ms is not None:
+        res["graph_step_GBs"] = nb["step"] / (graph_ms * 1e-3) / 1e9
+        res["graph_step_frac_of_peak"] = res["graph_step_GBs"] / PEAK_HBM_GBS
     if w.q_lens is not None:
         # a prefill chunk leans on the matrix cores: algorithmic flops of the
         # attention call against the dense bf16 peak
@@ -197,6 +340,8 @@ def measure(name, steps, warmup, dev, kernel=0, num_splits=0):
         res["attn_frac_of_bf16_peak"] = res["attn_TFLOPs"] / PEAK_BF16_TFLOPS
     del L
     torch.cuda.empty_cache()
+    if oracle_budget:
+        res["oracle"] = oracle_rate(w, oracle_budget)
     return w, res
 
 
@@ -259,7 +404,7 @@ def cpu_baseline(w, budget_s=12.0):
         oc = oracle.OracleCache(num_seqs=s.num_seqs, q_tokens=s.q_tokens, n_q_heads=s.n_q_heads,
                                 n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, block_size=s.block_size,
                                 k_pool=w.k_pool, v_pool=w.v_pool, block_table=w.block_table,
-                                seq_lens=w.seq_lens, cache_dtype=dt)
+                                seq_lens=w.seq_lens, cache_dtype=dt, q_lens=w.q_lens)
         t1 = time.perf_counter()
         oc.decode_attention(oc.rope_append_kv(w.q, w.k, w.v, s.rope_base, s.layout))
         reps += 1
@@ -267,7 +412,7 @@ def cpu_baseline(w, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s or reps >= 50:
             break
     elapsed = time.perf_counter() - t0
-    tokens = s.num_seqs * s.q_tokens * reps
+    tokens = (int(w.q_lens.sum()) if w.q_lens is not None else s.num_seqs * s.q_tokens) * reps
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{reps} full {s.name} step(s) (RoPE+append+attention, all {s.num_seqs * s.q_tokens} "
                       f"query tokens), fp64, OpenMP over query rows; last rep {t_work:.2f} s"}
@@ -422,6 +567,10 @@ def summarize(prof_dir, workload, commands):
         json.dump(allt, f, indent=1, sort_keys=True)
 
 
+def rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -430,8 +579,11 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=workloads.CONFIG_ORDER)
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--reps", type=int, default=REPS, help="repetitions of 20 calls per median")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip every CPU oracle timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replays")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="PROFILE_DIR",
                     help="write the profile summary of rocprofv3 output in PROFILE_DIR and exit")
@@ -453,52 +605,73 @@ def main():
     kb.lib()
     if args.calibrate_copy:
         copy_calibration(dev)
+    probe = None if args.no_probe else stream_probe(dev)
+    print(f"[bench] probe {probe and probe['GBs']} GB/s", file=sys.stderr, flush=True)
 
-    w, head = measure(args.workload, args.steps, args.warmup, dev, args.kernel, args.splits)
+    w, head = measure(args.workload, args.steps, args.warmup, dev, args.kernel, args.splits, args.reps,
+                      graph=not args.no_graph, contract=True, oracle_budget=0)
+    print(f"[bench] {args.workload}: {head['contract_step_ms']:.4f} ms per step", file=sys.stderr, flush=True)
     extra = {}
     if not args.no_extra:
         for name in workloads.CONFIG_ORDER:
             if name == args.workload:
                 continue
-            steps = max(10, args.steps // 4)
-            _, r = measure(name, steps, max(2, args.warmup // 4), dev, args.kernel, args.splits)
-            extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+            _, r = measure(name, 0, 0, dev, args.kernel, args.splits, args.reps, graph=not args.no_graph,
+                           oracle_budget=0 if args.no_cpu else 3.0)
+            extra[name] = rounded(r)
+            print(f"[bench] {name}: {r['step_ms']:.4f} ms per step", file=sys.stderr, flush=True)
         extra["long_ctx_cp8_shard"] = measure_cp_shard(max(10, args.steps // 4), max(2, args.warmup // 4), dev)
     cpu = None if args.no_cpu else cpu_baseline(w)
+    if probe:
+        for r in [head] + [r for r in extra.values() if "step_GBs" in r]:
+            r["step_frac_of_probe"] = round(r["step_GBs"] / probe["GBs"], 4)
+            r["attn_frac_of_probe"] = round(r["attn_GBs"] / probe["GBs"], 4)
 
     s = w.spec
+    tokens = int(w.q_lens.sum()) if w.q_lens is not None else s.num_seqs * s.q_tokens
+    step_ms = head["contract_step_ms"]
+    achieved = head["step_bytes"] / (step_ms * 1e-3) / 1e9
     traffic = stored_traffic(args.workload)
     line = {
         "metric": "decode-attention tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
-        "value": head["tokens_per_s"],
+        "value": tokens / (step_ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["step_ms"],
+        "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 cache, fp32 accumulate" if s.kv_dtype == "bf16" else "fp32",
-        "data": "synthetic (seeded; N(0,1)/sqrt(128) values, in-order paged table)",
-        "config": {"workload": f"{s.name}: decode step of one attention layer, B={s.num_seqs} T={s.q_tokens} "
-                               f"Hq={s.n_q_heads} Hkv={s.n_kv_heads} D={s.head_dim} context={w.max_seq_len - s.q_tokens} "
-                               f"bs={s.block_size} {s.kv_dtype}",
-                   "batch": s.num_seqs, "q_tokens_per_seq": s.q_tokens, "context": int(w.max_seq_len - s.q_tokens),
-                   "layers_rotated": head["layers_rotated"], "plan": head["plan"]},
-        "roofline": {"bound": "hbm", "achieved": head["step_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": head["step_GBs"] / PEAK_HBM_GBS, "traffic": traffic,
+        "data": head["data"],
+        "config": {"workload": head["workload"], "batch": s.num_seqs, "q_tokens_per_seq": s.q_tokens,
+                   "context": int(w.max_seq_len - s.q_tokens), "layers_rotated": head["layers_rotated"],
+                   "plan": head["plan"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "kvd_decode_step (fused RoPE + append + split-K attention kernel, "
                                "then the split combine)",
-                     "algorithmic_bytes_per_launch": head["step_bytes"], "avg_launch_ms": head["step_ms"]},
+                     "algorithmic_bytes_per_launch": head["step_bytes"], "avg_launch_ms": step_ms,
+                     "frac_of_probe": round(achieved / probe["GBs"], 4) if probe else None},
+        "median_of_reps": {"step_ms": head["step_ms"], "step_ms_spread": head["step_ms_spread"],
+                           "step_frac_of_peak": head["step_frac_of_peak"],
+                           "step_frac_of_probe": head.get("step_frac_of_probe"),
+                           "graph_step_ms": head["graph_step_ms"],
+                           "graph_step_frac_of_peak": head.get("graph_step_frac_of_peak"),
+                           "reps": args.reps, "calls_per_rep": CALLS},
         "two_call_step_ms": head["two_call_step_ms"],
         "attention_call": {"ms": head["attn_ms"], "GBs": head["attn_GBs"],
                            "frac": head["attn_frac_of_peak"], "algorithmic_bytes": head["attn_bytes"],
                            "tokens_per_s": head["attn_tokens_per_s"]},
+        "stream_probe": probe and {k: v for k, v in probe.items() if k != "sweep"},
         "cpu_baseline": cpu,
         "other_workloads": extra,
     }
     print(json.dumps(line), flush=True)
+    if probe and os.environ.get("KVD_BENCH_PROBE_SWEEP"):
+        with open(os.environ["KVD_BENCH_PROBE_SWEEP"], "w") as f:
+            json.dump(probe, f, indent=1)
 
 
 if __name__ == "__main__":

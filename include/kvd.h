@@ -103,11 +103,14 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *                       means key_pos0 = 0 and q_pos = key_pos0 +
  *                       seq_lens - T, the whole cache; with q_pos given,
  *                       seq_lens[b] may be below T (a shard without the new
- *                       tokens).  kvd_rope_append_kv rotates at the global
- *                       position and stores at local slot q_pos[b] + t -
- *                       key_pos0[b], which must lie in [0, seq_lens[b]).  A
- *                       row that sees no key of the shard gets out = 0 (and
- *                       lse = -inf from kvd_decode_attention_lse).
+ *                       tokens).  kvd_rope_append_kv (and kvd_decode_step)
+ *                       rotate at the global position and store at local
+ *                       slot q_pos[b] + t - key_pos0[b] when it lies in
+ *                       [0, seq_lens[b]); a shard that does not hold the
+ *                       slot gets the rotated query and stores nothing (the
+ *                       shard holding the token appends it).  A row that
+ *                       sees no key of the shard gets out = 0 (and lse =
+ *                       -inf from kvd_decode_attention_lse).
  *   q_lens              int32 [B] device array or NULL (= T for every
  *                       sequence): ragged chunks, sequence b brings q_lens[b]
  *                       <= T new tokens (chunked prefill with a different

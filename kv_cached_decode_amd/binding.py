@@ -25,9 +25,11 @@ KVD_KERNEL_AUTO, KVD_KERNEL_VALU, KVD_KERNEL_MFMA = 0, 1, 2
 EXPORTED = [
     "kvd_rope_append_kv", "kvd_decode_attention", "kvd_decode_attention_ex",
     "kvd_decode_attention_workspace_size", "kvd_decode_attention_workspace_size_ex",
-    "kvd_decode_attention_plan", "kvd_decode_step", "kvd_decode_attention_lse", "kvd_merge_partials",
-    "kvd_status_string", "kvd_last_error", "kvd_abi_version",
+    "kvd_decode_attention_plan", "kvd_decode_step",
+    "kvd_decode_attention_lse", "kvd_merge_partials", "kvd_status_string", "kvd_last_error",
+    "kvd_abi_version", "kvd_probe_stream_read",
 ]
+
 
 
 class KvdPagedKV(ctypes.Structure):
@@ -102,6 +104,8 @@ def lib():
         L.kvd_last_error.argtypes = []
         L.kvd_last_error.restype = ctypes.c_char_p
         L.kvd_abi_version.restype = I32
+        L.kvd_probe_stream_read.argtypes = [P, SZ, I32, I32, I32, P, P]
+        L.kvd_probe_stream_read.restype = I32
         _lib = L
     return _lib
 
@@ -260,19 +264,34 @@ def decode_attention_plan(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO):
 _ws_cache = {}
 
 
-def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO):
+def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO, stream=None):
     """A cached device workspace big enough for this descriptor (None if none
-    is needed).  Allocation happens here, outside the library; its contents
-    need no initialisation."""
+    is needed), one per (device, stream): calls that share a workspace must
+    not run concurrently, so work on different streams gets different
+    buffers.  The buffer is allocated on that stream (torch's allocator then
+    reuses a replaced one only for work ordered after it there).  Allocation
+    happens here, outside the library; the contents need no initialisation."""
     n = decode_attention_workspace_size(kv, num_splits, kernel)
     if n == 0:
         return None
     dev = kv.k_cache.device
-    buf = _ws_cache.get(dev)
+    handle = _stream_handle(stream)
+    key = (dev, handle)
+    buf = _ws_cache.get(key)
     if buf is None or buf.numel() < n:
-        buf = torch.zeros(n, dtype=torch.uint8, device=dev)
-        _ws_cache[dev] = buf
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        with torch.cuda.stream(s) if isinstance(s, torch.cuda.Stream) else _nullcontext():
+            buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
     return buf
+
+
+class _nullcontext:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
 
 
 def decode_attention(kv: PagedKV, q_rot, out=None, softmax_scale=0.0, workspace_buf=None,
@@ -284,7 +303,7 @@ def decode_attention(kv: PagedKV, q_rot, out=None, softmax_scale=0.0, workspace_
         out = torch.empty_like(q_rot)
     _need(out, "out", torch.float32, kv.q_shape())
     if workspace_buf is None:
-        workspace_buf = workspace(kv, num_splits, kernel)
+        workspace_buf = workspace(kv, num_splits, kernel, stream)
     wptr = workspace_buf.data_ptr() if workspace_buf is not None else None
     wbytes = workspace_buf.numel() * workspace_buf.element_size() if workspace_buf is not None else 0
     d = kv.struct()
@@ -312,7 +331,7 @@ def decode_step(kv: PagedKV, q, k, v, out=None, q_rot=None, want_q_rot=False, ro
     if q_rot is not None:
         _need(q_rot, "q_rot", torch.float32, kv.q_shape())
     if workspace_buf is None:
-        workspace_buf = workspace(kv, num_splits, kernel)
+        workspace_buf = workspace(kv, num_splits, kernel, stream)
     wptr = workspace_buf.data_ptr() if workspace_buf is not None else None
     wbytes = workspace_buf.numel() * workspace_buf.element_size() if workspace_buf is not None else 0
     d = kv.struct()
@@ -336,7 +355,7 @@ def decode_attention_lse(kv: PagedKV, q_rot, out=None, lse=None, softmax_scale=0
     _need(out, "out", torch.float32, kv.q_shape())
     _need(lse, "lse", torch.float32, kv.q_shape()[:3])
     if workspace_buf is None:
-        workspace_buf = workspace(kv, num_splits, kernel)
+        workspace_buf = workspace(kv, num_splits, kernel, stream)
     wptr = workspace_buf.data_ptr() if workspace_buf is not None else None
     wbytes = workspace_buf.numel() * workspace_buf.element_size() if workspace_buf is not None else 0
     d = kv.struct()
@@ -366,3 +385,18 @@ def merge_partials(outs, lses, out=None, lse_out=None, stream=None):
                                     lse_out.data_ptr(), _stream_handle(stream)),
            "kvd_merge_partials")
     return out, lse_out
+
+
+def probe_stream_read(buf, workgroups, threads=256, unroll=4, sink=None, stream=None):
+    """kvd_probe_stream_read (include/kvd_probe.h): one read of the whole of
+    `buf` (a contiguous device tensor) by a plain streaming kernel."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().kvd_probe_stream_read(buf.data_ptr(), nbytes, int(workgroups), int(threads), int(unroll),
+                                     sink.data_ptr(), _stream_handle(stream))
+    if st != 0:
+        raise RuntimeError(f"kvd_probe_stream_read failed with code {st}")
+    return sink

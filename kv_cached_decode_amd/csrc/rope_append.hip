@@ -5,7 +5,8 @@
 //
 // Grid: (new token (b, t), group of heads).  The token's position is
 // seq_lens[b] - n_new + t; in a context-parallel shard it is q_pos[b] + t,
-// stored at local slot q_pos[b] + t - key_pos0[b].  The D/2 rotation angles
+// stored at local slot q_pos[b] + t - key_pos0[b] if the shard holds that
+// slot (0 .. seq_lens[b] - 1), and not stored otherwise.  The D/2 rotation angles
 // pos * theta_i (theta_i = base^(-2i/D) from the host) are evaluated in fp64
 // once per workgroup and shared through LDS; every head's pair is then
 // rotated in fp64 and rounded once: to fp32 for q_rot and an fp32 cache, to
@@ -99,10 +100,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a, int 
         x[r].b = *(const float4*)(src + offb);
     }
     // the token's local slot, and its global position for the rotation (they
-    // differ in a context-parallel shard)
-    const int local = q_local0(c, b, c.seq_lens[b]) + t;
+    // differ in a context-parallel shard).  A shard whose keys do not include
+    // the slot rotates the query and stores nothing (the shard holding the
+    // token appends it), so neither the table nor the pools are touched.
+    const int L = c.seq_lens[b];
+    const int local = q_local0(c, b, L) + t;
     const int pos = local + (c.key_pos0 ? c.key_pos0[b] : 0);
-    const int blk = c.table[(size_t)b * c.max_blocks + (local >> c.log2_bs)];
+    const bool held = local >= 0 && local < L;
+    const int blk = held ? c.table[(size_t)b * c.max_blocks + (local >> c.log2_bs)] : 0;
 
     for (int p = threadIdx.x; p < half; p += blockDim.x)
         rope_angle(kernarg_double(offsetof(RopeAppendArgs, theta), p), pos, cs[p], sn[p]);
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a, int 
             *(float4*)(dst + offb) = y.b;
             continue;
         }
+        if (!held) continue;
         const bool is_k = hd < c.Hq + c.Hkv;
         const int h = is_k ? hd - c.Hq : hd - c.Hq - c.Hkv;
         const size_t row = ((((size_t)blk * c.Hkv + h) << c.log2_bs) + off) * D;

@@ -225,17 +225,18 @@ int oracle_rope_append_kv(const oracle_cache *c, const float *q,
         for (int32_t t = 0; t < n_new(c, b); ++t) {
             int64_t pos = q_pos0(c, b) + t;              /* global: the rotation */
             int64_t local = pos - key_pos0(c, b);        /* the cache slot */
-            if (local < 0 || local >= c->seq_lens[b]) {
-                free(x);
-                free(y);
-                return 1;
-            }
             for (int32_t h = 0; h < Hq; ++h) {
                 size_t o = (((size_t)b * T + t) * Hq + h) * D;
                 for (int32_t d = 0; d < D; ++d)
                     x[d] = (double)q[o + d];
                 rope_one(x, q_rot + o, D, pos, base, layout);
             }
+            /* a context-parallel shard that does not hold this token (its
+             * slot lies outside the keys the shard keeps) needs the rotated
+             * query for its partial but stores nothing: the shard holding
+             * the token appends it */
+            if (local < 0 || local >= c->seq_lens[b])
+                continue;
             for (int32_t h = 0; h < Hkv; ++h) {
                 size_t o = (((size_t)b * T + t) * Hkv + h) * D;
                 size_t s = slot_index(c, b, local, h);

@@ -86,7 +86,9 @@ int oracle_rope(const double *x, double *y, int32_t n_rows, int32_t n_heads,
 /* RoPE the new q and k at their global position p = q_pos[b] + t (default
  * seq_lens[b] - T + t), store round(k_rot) and round(v) into the slot of
  * local key p - key_pos0[b] that the block table names, and return the
- * rotated q in fp64.  q: [B][T][Hq][D]; k, v: [B][T][Hkv][D]; q_rot:
+ * rotated q in fp64.  A token whose local slot lies outside 0 .. seq_lens[b]
+ * - 1 (a context-parallel shard that does not hold it) is rotated into q_rot
+ * and not stored.  q: [B][T][Hq][D]; k, v: [B][T][Hkv][D]; q_rot:
  * [B][T][Hq][D]. */
 int oracle_rope_append_kv(const oracle_cache *c, const float *q,
                           const float *k, const float *v, double *q_rot,

@@ -532,7 +532,8 @@ def check_context_parallel_shards_merge_to_whole():
 def check_shard_append_rotates_at_global_position():
     """The shard holding a sequence's tail appends its new tokens at their
     global positions (the rotation) into its local slots: the stored rows and
-    q_rot equal the whole-cache append's bit for bit."""
+    q_rot equal the whole-cache append's bit for bit.  A shard without the
+    new tokens returns the same q_rot and leaves its pools untouched."""
     for dtype, kvd in (("f64", "f64"), ("bf16", "bf16")):
         spec = workloads.Spec("shard_append", 3, 2, 4, 2, 16, 4, kvd if kvd == "bf16" else "f32",
                               (5, 50), 10000.0, "normal", "shuffled", spare_frac=0.2, seed=24)
@@ -555,6 +556,14 @@ def check_shard_append_rotates_at_global_position():
                 a = whole.v_pool[w.block_table[b, gpos // bs], :, gpos % bs]
                 c = tail.v_pool[tail.block_table[b, loc // bs], :, loc % bs]
                 assert np.array_equal(a, c), (dtype, b, t)
+        # a shard that does not hold the new tokens (the head of every
+        # sequence) rotates the queries alike and stores nothing
+        head = _shard_cache(w, oracle_cache(w, dtype=dtype), np.zeros_like(cut), cut, dtype=dtype)
+        k_before, v_before = head.k_pool.copy(), head.v_pool.copy()
+        q_head = head.rope_append_kv(w.q, w.k, w.v, spec.rope_base)
+        assert np.array_equal(q_whole, q_head)
+        assert np.array_equal(head.k_pool.view(np.uint8), k_before.view(np.uint8))
+        assert np.array_equal(head.v_pool.view(np.uint8), v_before.view(np.uint8))
 
 
 def check_ragged_new_tokens():

@@ -10,15 +10,19 @@ import pytest
 from kv_cached_decode_amd import binding as kb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvd.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(kb.LIB_PATH), reason="libkvd.so not built")
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvd_[a-z0-9_]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(kvd_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
@@ -244,3 +248,4 @@ def test_prefill_plan(T):
     assert kern == 2 and s * k >= 4096 + T and (s - 1) * k < 4096 + T
     d = desc(num_seqs=2, q_tokens_per_seq=T, max_seq_len=1, q_lens=FAKE + 0x60000)
     assert _plan(d)[0] >= 1
+

@@ -182,3 +182,38 @@ def test_merge_of_many_parts(P):
     assert np.all(out[~live] == 0.0) and np.all(np.isneginf(mlse[~live]))
     assert np.max(np.abs(out[live] - ref[live])) <= 1e-5 * np.max(np.abs(ref[live]))
     assert np.max(np.abs(mlse[live] - (M + np.log(np.where(S > 0, S, 1.0)))[live])) <= 1e-5
+
+
+@pytest.mark.parametrize("name,kernel", [("mtp_verify", kb.KVD_KERNEL_AUTO), ("llama3_8b", kb.KVD_KERNEL_VALU)])
+def test_every_shard_runs_the_whole_step(name, kernel):
+    """Each shard calls kvd_decode_step with the same new tokens, as every GPU
+    of a context-parallel group would: the shards that do not hold the new
+    tokens rotate the queries and store nothing, the tail shard appends, so
+    the pools end exactly as the oracle's whole-cache append leaves them, and
+    each shard's output is its partial over the keys it holds."""
+    spec = workloads.small_variant(name)
+    w = cached_workload(spec)
+    note("every shard steps", name, kernel)
+    case = GpuCase(w)
+    P = 3
+    cuts = shard_cuts(w, P, seed=11)
+    kvs = [shard_kv(case, cuts, k) for k in range(P)]
+    oc = oracle_cache(w)
+    q_ref = oc.rope_append_kv(w.q, w.k, w.v, spec.rope_base, spec.layout)
+    for k, (kv, table, n) in enumerate(kvs):
+        out, q_rot = kb.decode_step(kv, case.q, case.k, case.v, q_rot=torch.zeros_like(case.q),
+                                    rope_base=spec.rope_base, layout=spec.layout, kernel=kernel)
+        torch.cuda.synchronize()
+        q_rot = q_rot.cpu().numpy()
+        assert np.max(np.abs(q_rot - q_ref) / (np.abs(q_ref) + 1e-30)) <= 2.0 ** -23, k
+        sh_oc = oracle_cache(w, seq_lens=n, block_table=table.clip(min=0), k_pool=oc.k_pool,
+                             v_pool=oc.v_pool, key_pos0=cuts[:, k],
+                             q_pos=w.seq_lens.astype(np.int64) - spec.q_tokens)
+        o_ref, l_ref = sh_oc.decode_attention(q_ref, want_lse=True)
+        out = out.cpu().numpy()
+        empty = np.isneginf(l_ref)
+        assert np.all(out[empty] == 0.0)
+        if (~empty).any():
+            assert_parity(spec, out[~empty], o_ref[~empty])
+    kp, vp = case.pools()
+    assert np.array_equal(kp, oc.k_pool) and np.array_equal(vp, oc.v_pool)
