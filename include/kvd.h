@@ -279,6 +279,32 @@ int32_t kvd_decode_step(const kvd_paged_kv *kv, const float *q, const float *k, 
                         float softmax_scale, const kvd_attn_options *opt, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/*
+ * kvd_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * split-K partials go to a static device array of KVD_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on (until the process ends)
+ * instead of a caller's workspace; nothing is allocated or freed.
+ *
+ *   Arguments and results as for kvd_decode_step, without the workspace.
+ *   A plan needing more partial storage than KVD_NOALLOC_SCRATCH_BYTES
+ *   (kvd_decode_attention_workspace_size_ex reports it) returns
+ *   KVD_ERR_WORKSPACE and enqueues nothing.  A plan with several splits
+ *   takes (head_dim + 2) * 4 bytes per (query row, split) pair, so 8 MiB
+ *   holds about 16000 pairs at head_dim 128; plans of one split need none.
+ *   Every call on one GPU shares that GPU's array, and each call rewrites
+ *   every partial it reads (nothing needs clearing between calls), so calls
+ *   that may overlap on one GPU -- on different streams, or from different
+ *   host threads without ordering -- race and must not be issued.
+ *   The first call on a device looks the array's address up (a runtime query,
+ *   no allocation); a failure there returns KVD_ERR_LAUNCH.
+ */
+#define KVD_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t kvd_decode_step_noalloc(const kvd_paged_kv *kv, const float *q, const float *k,
+                                const float *v, float *q_rot, float *out, double rope_base,
+                                int32_t layout, float softmax_scale, const kvd_attn_options *opt,
+                                void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kvd_status_string(int32_t status);
 

@@ -25,11 +25,13 @@ KVD_KERNEL_AUTO, KVD_KERNEL_VALU, KVD_KERNEL_MFMA = 0, 1, 2
 EXPORTED = [
     "kvd_rope_append_kv", "kvd_decode_attention", "kvd_decode_attention_ex",
     "kvd_decode_attention_workspace_size", "kvd_decode_attention_workspace_size_ex",
-    "kvd_decode_attention_plan", "kvd_decode_step",
+    "kvd_decode_attention_plan", "kvd_decode_step", "kvd_decode_step_noalloc",
     "kvd_decode_attention_lse", "kvd_merge_partials", "kvd_status_string", "kvd_last_error",
     "kvd_abi_version", "kvd_probe_stream_read",
 ]
 
+# bytes of the per-device static scratch of kvd_decode_step_noalloc (kvd.h)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class KvdPagedKV(ctypes.Structure):
@@ -95,6 +97,9 @@ def lib():
         L.kvd_decode_step.argtypes = [KV, P, P, P, P, P, ctypes.c_double, I32, ctypes.c_float, OPT,
                                       P, SZ, P]
         L.kvd_decode_step.restype = I32
+        L.kvd_decode_step_noalloc.argtypes = [KV, P, P, P, P, P, ctypes.c_double, I32, ctypes.c_float,
+                                              OPT, P]
+        L.kvd_decode_step_noalloc.restype = I32
         L.kvd_decode_attention_lse.argtypes = [KV, P, P, P, ctypes.c_float, OPT, P, SZ, P]
         L.kvd_decode_attention_lse.restype = I32
         L.kvd_merge_partials.argtypes = [I32, ctypes.c_int64, I32, P, P, P, P, P]
@@ -341,6 +346,28 @@ def decode_step(kv: PagedKV, q, k, v, out=None, q_rot=None, want_q_rot=False, ro
                                  _opts(num_splits, kernel), wptr, wbytes, _stream_handle(stream)),
            "kvd_decode_step")
     return (out, q_rot) if q_rot is not None else out
+
+
+def decode_step_noalloc(kv: PagedKV, q, k, v, out, q_rot=None, rope_base=10000.0,
+                        layout=KVD_ROPE_HALF, softmax_scale=0.0, num_splits=0,
+                        kernel=KVD_KERNEL_AUTO, stream=None):
+    """kvd_decode_step_noalloc: the whole step with the split-K partials in
+    the library's static per-device scratch; the caller passes every output
+    buffer (nothing is allocated here either).  Returns out."""
+    _need(q, "q", torch.float32, kv.q_shape())
+    _need(k, "k", torch.float32, kv.kv_shape())
+    _need(v, "v", torch.float32, kv.kv_shape())
+    _need(out, "out", torch.float32, kv.q_shape())
+    if q_rot is not None:
+        _need(q_rot, "q_rot", torch.float32, kv.q_shape())
+    d = kv.struct()
+    _check(lib().kvd_decode_step_noalloc(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         q_rot.data_ptr() if q_rot is not None else None,
+                                         out.data_ptr(), float(rope_base), int(layout),
+                                         float(softmax_scale), _opts(num_splits, kernel),
+                                         _stream_handle(stream)),
+           "kvd_decode_step_noalloc")
+    return out
 
 
 def decode_attention_lse(kv: PagedKV, q_rot, out=None, lse=None, softmax_scale=0.0, workspace_buf=None,

@@ -13,6 +13,13 @@
 
 #include "kvd_internal.h"
 
+// Split-K scratch of kvd_decode_step_noalloc: one array per device (each
+// GPU that loads the library holds its own copy until the process ends).  In
+// host code `scratch` is only a stand-in for the symbol; the device address
+// comes from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is ever passed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[KVD_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -370,11 +377,61 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
     return ok();
 }
 
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {nullptr};
+
+// The device address of the current device's scratch array in *ptr (the
+// first call on a device looks it up with that device current).
+int32_t scratch_ptr(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return fail(KVD_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KVD_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return KVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t kvd_abi_version(void) { return 3; }
+
+int32_t kvd_decode_step_noalloc(const kvd_paged_kv* kv, const float* q, const float* k,
+                                const float* v, float* q_rot, float* out, double rope_base,
+                                int32_t layout, float softmax_scale, const kvd_attn_options* opt,
+                                void* stream) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (kv->num_seqs == 0) return ok();
+    Plan p;
+    st = make_plan(kv, opt, &p);
+    if (st != KVD_OK) return st;
+    const size_t need = workspace_for(kv, p);
+    if (need > (size_t)KVD_NOALLOC_SCRATCH_BYTES)
+        return fail(KVD_ERR_WORKSPACE,
+                    "the plan needs %zu bytes of split-K scratch, above the %zu of the static scratch "
+                    "(use kvd_decode_step with a workspace, or fewer splits)",
+                    need, (size_t)KVD_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_ptr(&ws);
+        if (st != KVD_OK) return st;
+    }
+    return kvd_decode_step(kv, q, k, v, q_rot, out, rope_base, layout, softmax_scale, opt, ws,
+                           need > 0 ? (size_t)KVD_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
 
 int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, const float* v,
                         float* q_rot, float* out, double rope_base, int32_t layout,

@@ -249,3 +249,28 @@ def test_prefill_plan(T):
     d = desc(num_seqs=2, q_tokens_per_seq=T, max_seq_len=1, q_lens=FAKE + 0x60000)
     assert _plan(d)[0] >= 1
 
+
+def test_noalloc_step_validates_before_anything_runs():
+    """kvd_decode_step_noalloc checks like kvd_decode_step, then refuses a plan
+    whose split-K partials exceed its static scratch (KVD_NOALLOC_SCRATCH_BYTES)
+    before it looks up the scratch or launches anything."""
+    L = kb.lib()
+
+    def step(d, splits=0):
+        opt = ctypes.byref(kb.KvdAttnOptions(splits, 0)) if splits else None
+        return L.kvd_decode_step_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 1e4, 0, 0.0, opt,
+                                         None)
+
+    assert L.kvd_decode_step_noalloc(None, FAKE, FAKE, FAKE, None, FAKE, 1e4, 0, 0.0, None,
+                                     None) == kb.KVD_ERR_NULL
+    for kw, status in BAD:
+        assert step(desc(**kw)) == status, (kw, kb.last_error())
+    assert step(desc(num_seqs=0, k_cache=0, v_cache=0, block_table=0, seq_lens=0)) == kb.KVD_OK
+    # the full continuous batch (64 sequences x 16 q heads, up to 8193 keys)
+    # at 20 splits: 1024 rows x 20 x (128 + 2) x 4 bytes = 10.6 MB > 8 MiB
+    big = desc(num_seqs=64, n_q_heads=16, n_kv_heads=8, max_blocks_per_seq=513, max_seq_len=8193,
+               num_blocks=40000)
+    need = L.kvd_decode_attention_workspace_size_ex(ctypes.byref(big), ctypes.byref(kb.KvdAttnOptions(20, 0)))
+    assert need > kb.NOALLOC_SCRATCH_BYTES
+    assert step(big, 20) == kb.KVD_ERR_WORKSPACE
+    assert "static scratch" in kb.last_error()
