@@ -464,14 +464,16 @@ def _median(v):
     return v[len(v) // 2] if v else float("nan")
 
 
-def summarize(prof_dir, workload, commands):
+def summarize(prof_dir, workload, commands, record=True):
     """Turn rocprofv3 CSV output (kt/ kernel trace, fetch/ FETCH_SIZE,
-    write/ WRITE_SIZE, util/ utilisation counters) into a markdown summary on
-    stdout and record the calibrated traffic per decode-attention call."""
+    write/ WRITE_SIZE, util/ utilisation counters, tcc/ L2 hits and misses)
+    into a markdown summary on stdout and, with `record` (runs of the
+    automatic plan), record the calibrated traffic per call."""
     import collections
     w = workloads.make_workload(workloads.CONFIGS[workload])
     alg = w.algorithmic_bytes()
-    out = [f"# {workload}: decode-step kernels on MI355X (rocprofv3)", ""]
+    out = [f"# {workload}: decode-step kernels on MI355X (rocprofv3)", "",
+           workload_text(w), "", describe_data(w.spec), ""]
     out += ["Commands (repository root):", "", "```"] + commands + ["```", ""]
 
     trace = _csv_rows(os.path.join(prof_dir, "kt"), "kernel_trace.csv")
@@ -531,6 +533,20 @@ def summarize(prof_dir, workload, commands):
             f"Decode-attention call alone: {traffic / 1e6:.2f} MB of HBM traffic vs "
             f"{alg['attention'] / 1e6:.2f} MB algorithmic ({traffic / alg['attention']:.3f}x).", ""]
 
+    tcc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv_rows(os.path.join(prof_dir, "tcc"), "counter_collection.csv"):
+        tcc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if tcc:
+        out += ["## L2 reuse (--pmc TCC_HIT_sum TCC_MISS_sum; requests per dispatch)", "",
+                "| kernel | TCC_HIT | TCC_MISS | hit rate |", "|---|---|---|---|"]
+        for k in sorted(tcc):
+            if not k.startswith(("attn_", "decode_step", "rope_append")):
+                continue
+            h = _median(tcc[k].get("TCC_HIT_sum", [0.0]))
+            m = _median(tcc[k].get("TCC_MISS_sum", [0.0]))
+            out.append(f"| {k} | {h:.0f} | {m:.0f} | {h / max(h + m, 1.0):.1%} |")
+        out.append("")
+
     util = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in _csv_rows(os.path.join(prof_dir, "util"), "counter_collection.csv"):
         util[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
@@ -553,6 +569,8 @@ def summarize(prof_dir, workload, commands):
         out.append("")
     print("\n".join(out))
 
+    if not record:
+        return
     entry = {"kernel_sources_sha": kernel_sources_sha(), "step_bytes_per_launch": round(step_traffic),
              "attn_bytes_per_launch": round(traffic), "fetch_factor": f_fac, "write_factor": w_fac,
              "step_us_trace": step_us, "attn_us_trace": attn_us}
@@ -591,7 +609,7 @@ def main():
                     help="(with --summarize) a profiling command to quote in the summary")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.workload, args.command)
+        summarize(args.summarize, args.workload, args.command, record=args.kernel == 0)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "

@@ -21,6 +21,9 @@ Workload shapes follow the five named configurations of the decode step:
 * ``chunked_prefill`` -- batch 8 of Llama-3-8B-shaped layers taking a prefill
   chunk each: ragged chunks of 64..512 new tokens (uniform per sequence) on
   ragged contexts uniform in [0, 4096], paged bf16 (block 16, shuffled).
+* ``llama2_7b_mha``  -- multi-head decode (one query head per kv head, the
+  case only the vector-ALU kernel serves): batch 16, 32 q = 32 kv heads,
+  head_dim 128, context 4096, paged bf16 (block 16, shuffled), values N(0,1).
 
 bf16 values are drawn as float32 and truncated to their top 16 bits (a
 distribution choice, not a rounding the method performs).  Cache slots past
@@ -82,8 +85,11 @@ CONFIGS = {
                        "shuffled", spare_frac=0.05, seed=5),
     "chunked_prefill": Spec("chunked_prefill", 8, 512, 32, 8, 128, 16, "bf16", (0, 4096), 500000.0,
                             "normal_scaled", "shuffled", spare_frac=0.05, seed=7, chunk=(64, 512)),
+    "llama2_7b_mha": Spec("llama2_7b_mha", 16, 1, 32, 32, 128, 16, "bf16", 4096, 10000.0, "normal",
+                          "shuffled", spare_frac=0.05, seed=8),
 }
-CONFIG_ORDER = ["tiny_f32", "llama3_8b", "qwen3_0_6b_cb", "long_ctx", "mtp_verify", "chunked_prefill"]
+CONFIG_ORDER = ["tiny_f32", "llama3_8b", "qwen3_0_6b_cb", "long_ctx", "mtp_verify", "chunked_prefill",
+                "llama2_7b_mha"]
 
 
 def small_variant(name: str) -> Spec:
@@ -103,6 +109,8 @@ def small_variant(name: str) -> Spec:
     if name == "chunked_prefill":
         return s.with_(name=name + "_small", num_seqs=3, q_tokens=96, ctx=(0, 300), chunk=(1, 96),
                        seed=107)
+    if name == "llama2_7b_mha":
+        return s.with_(name=name + "_small", num_seqs=3, ctx=(1, 900), seed=108)
     raise KeyError(name)
 
 
