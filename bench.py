@@ -122,12 +122,12 @@ class Layers:
             self.ws = self.ws.clone()
         self.plan = kb.decode_attention_plan(self.kv[0], num_splits, kernel)
         # The step's output is the attention output; the rotated queries are
-        # an intermediate.  A matrix-core decode plan runs as one kernel and
-        # needs no buffer for them; the other plans (prefill tiles, the
-        # vector-ALU kernel) run the two kernels in a row and get one, as a
-        # caller would pass it, rather than reusing `out`.
-        rows = s.n_q_heads // s.n_kv_heads * s.q_tokens
-        fused = self.plan[2] == kb.KVD_KERNEL_MFMA and rows <= 16
+        # an intermediate.  The matrix-core plans rotate them inside the
+        # attention kernel (the decode kernel also appends; the prefill kernel
+        # runs after the RoPE/append kernel has appended) and need no buffer
+        # for them; the vector-ALU plans run the two kernels in a row and get
+        # one, as a caller would pass it, rather than reusing `out`.
+        fused = self.plan[2] == kb.KVD_KERNEL_MFMA
         self.step_q_rot = None if fused else self.q_rot
 
     def step(self, i):
@@ -186,6 +186,10 @@ def graph_timed(fn, results, calls=CALLS, replays=REPS):
     of `fn` captured in one HIP graph, replayed `replays` times, each replay
     between its own HIP events; the median ms per call.  The graph's results
     must equal those of the same calls made eagerly (None otherwise)."""
+    # the same start for the eager calls and the replay (rows a call leaves
+    # as they are, such as padding rows, must match too)
+    for r in results:
+        r.zero_()
     for i in range(calls):
         fn(i)
     torch.cuda.synchronize()
@@ -198,7 +202,8 @@ def graph_timed(fn, results, calls=CALLS, replays=REPS):
             fn(i)
     torch.cuda.synchronize()
     for r in results:
-        r.fill_(float("nan"))
+        r.zero_()
+    torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
     if not all(torch.equal(r, e) for r, e in zip(results, eager)):

@@ -117,8 +117,8 @@ enum { KVD_KERNEL_AUTO = 0, KVD_KERNEL_VALU = 1, KVD_KERNEL_MFMA = 2 };
  *                       chunk per sequence, drafts of different lengths).
  *                       They are the last q_lens[b] keys (or sit at q_pos[b]
  *                       + t); rows t >= q_lens[b] are padding: not appended,
- *                       their q_rot rows left as they are and their out rows
- *                       0 (lse -inf).  seq_lens[b] >= q_lens[b].
+ *                       and their q_rot, out and lse rows are left as they
+ *                       are (not written).  seq_lens[b] >= q_lens[b].
  */
 typedef struct kvd_paged_kv {
     int32_t num_seqs;
@@ -269,10 +269,14 @@ int32_t kvd_merge_partials(int32_t n_parts, int64_t rows, int32_t head_dim, cons
  * kernel does all of it (plus the split combine when there are several
  * splits): each workgroup rotates its own query rows, and the workgroup whose
  * key range holds the new tokens stores their K/V rows and uses them directly.
- * Pass q_rot = NULL there unless the rotated queries are wanted: writing them
- * is extra work.  Otherwise the RoPE/append kernel runs first and, if q_rot is
- * NULL, `out` holds the rotated queries in between (measured about 7% slower
- * on a large prefill chunk than with a q_rot buffer).
+ * When it uses the prefill kernel (more than 16 query rows per kv head), the
+ * RoPE/append kernel appends the new K/V rows and the prefill kernel rotates
+ * the query rows it reads (the rotated queries make no round trip through
+ * memory).  On both, pass q_rot = NULL unless the rotated queries are
+ * wanted: writing them is extra work.  Otherwise (the vector-ALU kernel, or a
+ * context-parallel shard or long split on the decode kernel) the RoPE/append
+ * kernel runs first and, if q_rot is NULL, `out` holds the rotated queries in
+ * between.
  */
 int32_t kvd_decode_step(const kvd_paged_kv *kv, const float *q, const float *k, const float *v,
                         float *q_rot, float *out, double rope_base, int32_t layout,

@@ -225,6 +225,12 @@ class PagedKV:
         return (self.num_seqs, self.q_tokens_per_seq, self.n_kv_heads, self.head_dim)
 
 
+def _new_out(kv: PagedKV, like):
+    """An output buffer allocated here: zeros for a batch of ragged chunks,
+    whose padding rows the library leaves as they are (so they read as 0)."""
+    return torch.zeros_like(like) if kv.q_lens is not None else torch.empty_like(like)
+
+
 def _opts(num_splits, kernel):
     if not num_splits and not kernel:
         return None
@@ -305,7 +311,7 @@ def decode_attention(kv: PagedKV, q_rot, out=None, softmax_scale=0.0, workspace_
     keys query t of sequence b can see.  Returns out."""
     _need(q_rot, "q_rot", torch.float32, kv.q_shape())
     if out is None:
-        out = torch.empty_like(q_rot)
+        out = _new_out(kv, q_rot)
     _need(out, "out", torch.float32, kv.q_shape())
     if workspace_buf is None:
         workspace_buf = workspace(kv, num_splits, kernel, stream)
@@ -329,7 +335,7 @@ def decode_step(kv: PagedKV, q, k, v, out=None, q_rot=None, want_q_rot=False, ro
     _need(k, "k", torch.float32, kv.kv_shape())
     _need(v, "v", torch.float32, kv.kv_shape())
     if out is None:
-        out = torch.empty_like(q)
+        out = _new_out(kv, q)
     _need(out, "out", torch.float32, kv.q_shape())
     if q_rot is None and want_q_rot:
         q_rot = torch.empty_like(q)
@@ -376,9 +382,13 @@ def decode_attention_lse(kv: PagedKV, q_rot, out=None, lse=None, softmax_scale=0
     log-sum-exp (a context-parallel shard's partial).  Returns (out, lse)."""
     _need(q_rot, "q_rot", torch.float32, kv.q_shape())
     if out is None:
-        out = torch.empty_like(q_rot)
+        out = _new_out(kv, q_rot)
     if lse is None:
-        lse = torch.empty(kv.q_shape()[:3], dtype=torch.float32, device=q_rot.device)
+        shape = kv.q_shape()[:3]
+        if kv.q_lens is not None:      # padding rows are left as they are: -inf here
+            lse = torch.full(shape, float("-inf"), dtype=torch.float32, device=q_rot.device)
+        else:
+            lse = torch.empty(shape, dtype=torch.float32, device=q_rot.device)
     _need(out, "out", torch.float32, kv.q_shape())
     _need(lse, "lse", torch.float32, kv.q_shape()[:3])
     if workspace_buf is None:

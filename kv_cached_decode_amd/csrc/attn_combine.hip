@@ -10,7 +10,8 @@
 // Nothing here depends on the sequence lengths, so the merge costs one
 // memory round trip.
 //
-// Fixed summation order, so results are bitwise reproducible.
+// Fixed summation order, so results are bitwise reproducible.  Rows of
+// padding tokens past a ragged chunk are left as they are.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -23,6 +24,14 @@ namespace {
 // independent loads in flight.
 constexpr int COMBINE_THREADS = 128;
 constexpr int MAX_STAGED_SPLITS = 1024;
+
+// Query row (b*T + t)*Hq + h belongs to a padding token of a ragged chunk
+// (t >= q_lens[b]): its output is left as it is.
+__device__ inline bool is_padding(const CacheView& c, size_t qrow) {
+    if (!c.q_lens) return false;
+    const size_t bt = qrow / c.Hq;
+    return (int)(bt % c.T) >= c.q_lens[bt / c.T];
+}
 
 __device__ inline float wave_max(float x) {
 #pragma unroll
@@ -49,7 +58,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void attn_combine_rows_kernel(AttnArg
     const size_t rows = (size_t)c.B * c.T * c.Hq;
     const size_t qrow = (size_t)blockIdx.x * rpw + (threadIdx.x >> lq);
     const int e4 = threadIdx.x & ((1 << lq) - 1);
-    if (qrow >= rows) return;
+    if (qrow >= rows || is_padding(c, qrow)) return;
     const int n = a.num_splits;
     const float2* ml = (const float2*)(a.part_ml + qrow * n * 2);
     const float4* po = (const float4*)(a.part_o + qrow * n * c.D) + e4;
@@ -87,6 +96,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(AttnArgs 
     __shared__ float sm_red[2];
     const CacheView& c = a.c;
     const size_t qrow = blockIdx.x;                     // (b*T + t)*Hq + h
+    if (is_padding(c, qrow)) return;
     const int S = a.num_splits;
     const int n = S;
     const float* ml = a.part_ml + qrow * S * 2;

@@ -649,6 +649,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         const int h = kvh * c.g + (r - t * c.g);
         const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h;
         if (a.num_splits == 1) {
+            if (t >= nn) break;             // padding rows (past a ragged chunk) are left as they are
             a.out[qrow * D + d] = finish_out(O, Ls);
             if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
         } else {

@@ -25,12 +25,23 @@
 // the window of its first), and leaves out the mask on tiles every one of its
 // rows sees whole; the running rescale happens only when a row's maximum
 // grows (otherwise its factor is exactly 1).  Rows past the chunk take no
-// part and write the empty result.  Split ranges, windows, ragged chunks and
-// context-parallel shards follow the same rules as the decode kernels
-// (kvd_internal.h).
+// part, and their outputs are left as they are.  Split ranges, windows,
+// ragged chunks and context-parallel shards follow the same rules as the
+// decode kernels (kvd_internal.h).
+//
+// RoPE of the queries (rope_q: q holds the raw queries, the RoPE/append
+// kernel has appended the new K/V rows before this kernel runs): each query
+// row is rotated by the workgroup that reads it, at its token's position,
+// with the RoPE/append kernel's arithmetic (fp64 angle, cosine, sine and
+// rotation, rounded once to fp32), so the result is bitwise that of reading
+// its rotated queries.  The angles of the tile's tokens are formed once per
+// workgroup, 32 tokens at a time, in the LDS of the K/V tiles before the first
+// tile is staged; every lane holds both elements of each of its pairs (dims d
+// and d + 64, or 2i and 2i + 1), so the rotation needs no data exchange.
 #include <type_traits>
 
 #include "kvd_internal.h"
+#include "rope_math.h"
 
 namespace kvd {
 namespace {
@@ -57,6 +68,10 @@ constexpr int MAX_STAGED_BLOCKS = 4096;   // block ids of a split, staged in LDS
 constexpr int RANK_MAX = PREFILL_RANK_MAX;  // units ranked longest-first (their key counts and the units by rank share the block-id array)
 static_assert(RANK_MAX <= 256, "one unit per thread in the ranking");
 constexpr float M_EMPTY = -1e30f;
+constexpr int HALF = D / 2;
+constexpr int ANG_TOKENS = 32;            // tokens whose angles share the LDS at a time
+static_assert(2 * ANG_TOKENS * HALF * sizeof(double) <= 2 * K_BYTES + 2 * V_BYTES,
+              "the angle table fits in the K/V tiles");
 // The running maximum of a row moves (and its sums are rescaled) only when a
 // tile's scores exceed it by more than RESCALE_SLACK (log2 units); below that
 // the weights exp2(s - m) stay at most 2^RESCALE_SLACK, harmless in fp32, and
@@ -193,8 +208,11 @@ __device__ inline int cu_paired_rank(int pos, int n_units, int Hkv) {
 }
 
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char sm_k[2][K_BYTES];
-    __shared__ __attribute__((aligned(16))) char sm_v[2][V_BYTES];
+    // the K and V tiles (double-buffered); before the first tile, the
+    // cosines and sines of the query rotation
+    __shared__ __attribute__((aligned(16))) char sm_kv[2 * K_BYTES + 2 * V_BYTES];
+    char (*const sm_k)[K_BYTES] = (char (*)[K_BYTES])sm_kv;
+    char (*const sm_v)[V_BYTES] = (char (*)[V_BYTES])(sm_kv + 2 * K_BYTES);
     __shared__ __attribute__((aligned(16))) int sm_blk[MAX_STAGED_BLOCKS];
     __shared__ int sm_v_normal, sm_nonfinite;   // the fast pass's verdict
 
@@ -248,7 +266,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     const int row0 = un.rtile * ROWS;
     const int qo = un.qo, n_live = un.n_live, live_rows = un.live_rows;
     const int key_begin = un.key_begin, key_end = un.key_end;
-    if (live_rows <= 0 || key_begin >= key_end) {
+    // a unit without keys (a context-parallel shard holding none its rows
+    // see) still rotates its rows when the rotated queries are asked for
+    const bool no_keys = key_begin >= key_end;
+    if (live_rows <= 0 || (no_keys && !(a.rope_q && a.q_rot && split == 0))) {
         write_empty_partials(a, b, kvh, split, row0, ROWS);
         return;
     }
@@ -297,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         }
     }
     const int blk0 = key_begin >> c.log2_bs;
-    const int nblk = ((key_end - 1) >> c.log2_bs) - blk0 + 1;
+    const int nblk = no_keys ? 0 : ((key_end - 1) >> c.log2_bs) - blk0 + 1;
     const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
     // staged as the (block, kv head) row of the pools: blk * Hkv + kvh
     for (int i = tid; i < nblk; i += blockDim.x) sm_blk[i] = trow[i] * c.Hkv + kvh;
@@ -326,7 +347,83 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
             vr[i] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
         }
     };
-    load(key_begin);
+    if (!no_keys) load(key_begin);
+
+    if (a.rope_q) {
+        // The queries of the tile's tokens, rotated at their positions: the
+        // angles of up to ANG_TOKENS tokens at a time into LDS (thread tid
+        // keeps pair tid % HALF in every round), then each lane turns the
+        // pairs of its rows whose tokens are in the round.
+        double* const cs = (double*)sm_kv;
+        double* const sn = cs + ANG_TOKENS * HALF;
+        const double theta = kernarg_double(offsetof(AttnArgs, theta), tid % HALF);
+        const int pos0 = qo + (c.key_pos0 ? c.key_pos0[b] : 0);    // global position of token 0
+        const int t_lo = row0 / c.g;
+        const int t_hi = min(n_live - 1, row0 + ROWS - 1) / c.g + 1;
+        int t_row[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) t_row[rb] = row_live[rb] ? (wrow0 + 16 * rb + n16) / c.g : -1;
+        for (int tb = t_lo; tb < t_hi; tb += ANG_TOKENS) {
+            const int nt = min(ANG_TOKENS, t_hi - tb);
+            for (int idx = tid; idx < nt * HALF; idx += blockDim.x)
+                rope_angle(theta, pos0 + tb + idx / HALF, cs[idx], sn[idx]);
+            __syncthreads();
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int tt = t_row[rb] - tb;
+                if (tt < 0 || tt >= nt) continue;
+                const double* cr = cs + tt * HALF;
+                const double* sr = sn + tt * HALF;
+                auto turn = [&](float& x, float& y, int i) {
+                    double xr, yr;
+                    rope_rotate(x, y, cr[i], sr[i], xr, yr);
+                    x = (float)xr;
+                    y = (float)yr;
+                };
+                if (a.interleaved) {
+                    // pairs (2i, 2i + 1) inside each float4: dims 32kk + 8j + 4h + {0,1} and {2,3}
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int i = 16 * kk + 4 * j + 2 * h;
+                            turn(xq[rb][kk][h].x, xq[rb][kk][h].y, i);
+                            turn(xq[rb][kk][h].z, xq[rb][kk][h].w, i + 1);
+                        }
+                } else {
+                    // pairs (i, i + 64): dims 8j + e with 64 + 8j + e, and 32 + 8j + e with 96 + 8j + e
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int i = 32 * kk + 8 * j + 4 * h;
+                            turn(xq[rb][kk][h].x, xq[rb][kk + 2][h].x, i);
+                            turn(xq[rb][kk][h].y, xq[rb][kk + 2][h].y, i + 1);
+                            turn(xq[rb][kk][h].z, xq[rb][kk + 2][h].z, i + 2);
+                            turn(xq[rb][kk][h].w, xq[rb][kk + 2][h].w, i + 3);
+                        }
+                }
+            }
+            __syncthreads();          // the table is rewritten next round, then staged over
+        }
+        // the rotated queries, when asked for (split 0 writes them)
+        if (a.q_rot && split == 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                if (!row_live[rb]) continue;
+                float* qp = a.q_rot + qrow[rb] * D;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    *(float4*)(qp + 32 * kk + 8 * j) = xq[rb][kk][0];
+                    *(float4*)(qp + 32 * kk + 8 * j + 4) = xq[rb][kk][1];
+                }
+            }
+        }
+    }
+    if (no_keys) {
+        write_empty_partials(a, b, kvh, split, row0, ROWS);
+        return;
+    }
 
     // Q^T operands in log2 units, hi + lo
     bf16x8 qhi[RB][4], qlo[RB][4];
@@ -550,7 +647,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         if (!row_ok[rb]) continue;
-        if (!row_live[rb]) {        // a padding token: the empty result
+        if (!row_live[rb]) {        // a padding token: left as it is, or an empty partial
+            if (a.num_splits == 1) continue;
             m[rb] = M_EMPTY;
             lsum[rb] = 0.0f;
 #pragma unroll

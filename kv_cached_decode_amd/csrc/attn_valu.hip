@@ -299,6 +299,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         const int h = kvh * c.g + (row - t * c.g);
         const size_t qrow = ((size_t)b * c.T + t) * c.Hq + h;
         if (a.num_splits == 1) {
+            if (t >= nn) continue;          // padding rows (past a ragged chunk) are left as they are
             a.out[qrow * D + d] = finish_out(O, Ls);
             if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
         } else {

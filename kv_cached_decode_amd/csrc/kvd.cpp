@@ -287,11 +287,12 @@ int32_t check_rope(const float* q, const float* k, const float* v, const float* 
 }
 
 int32_t rope_append(const kvd_paged_kv* kv, const float* q, const float* k, const float* v,
-                    float* q_rot, double rope_base, int32_t layout, void* stream) {
+                    float* q_rot, double rope_base, int32_t layout, void* stream, bool skip_q = false) {
     kvd::RopeAppendArgs a;
     a.c = view_of(kv);
     a.kv_bf16 = kv->kv_dtype == KVD_KV_BF16;
     a.interleaved = layout == KVD_ROPE_INTERLEAVED;
+    a.skip_q = skip_q;
     fill_theta(&a.theta, rope_base, kv->head_dim);
     a.q = q;
     a.k = k;
@@ -302,13 +303,16 @@ int32_t rope_append(const kvd_paged_kv* kv, const float* q, const float* k, cons
     return ok();
 }
 
-// Inputs of the fused decode step (RoPE + append inside the attention kernel).
+// Inputs of the fused step: RoPE + append inside the decode attention kernel,
+// or (rope_q_only) the queries' RoPE inside the prefill kernel after the
+// RoPE/append kernel has appended the new K/V rows.
 struct FuseIn {
     const float* k;
     const float* v;
     float* q_rot;         // may be null
     double rope_base;
     int32_t layout;
+    bool rope_q_only;
 };
 
 // Decode attention; with `fuse`, q_rot is the raw q and the matrix-core
@@ -354,7 +358,8 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
     a.part_o = nullptr;
     a.part_ml = nullptr;
     a.lse = lse;
-    a.fused = fuse != nullptr;
+    a.fused = fuse != nullptr && !fuse->rope_q_only;
+    a.rope_q = fuse != nullptr && fuse->rope_q_only;
     a.interleaved = fuse && fuse->layout == KVD_ROPE_INTERLEAVED;
     if (fuse) fill_theta(&a.theta, fuse->rope_base, kv->head_dim);
     a.k_new = fuse ? fuse->k : nullptr;
@@ -450,13 +455,21 @@ int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, 
     const bool one_piece = (int64_t)p.split_keys + kv->block_size - 1 <=
                            (int64_t)kvd::MFMA_PIECE_BLOCKS * kv->block_size;
     if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && !kv->key_pos0 && !kv->q_pos && one_piece) {
-        const FuseIn f{k, v, q_rot, rope_base, layout};
+        const FuseIn f{k, v, q_rot, rope_base, layout, false};
         return attention(kv, q, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
     }
-    // vector-ALU and prefill plans, context-parallel shards and splits of
-    // more blocks than one piece: the two kernels in a row; `out` holds the
-    // rotated queries when the caller wants none back (each output row is
-    // written only after its query row has been read)
+    if (p.prefill) {
+        // the new K/V rows first (every row tile at or past them reads them),
+        // then the prefill kernel rotates its own query rows
+        st = rope_append(kv, q, k, v, nullptr, rope_base, layout, stream, true);
+        if (st != KVD_OK) return st;
+        const FuseIn f{k, v, q_rot, rope_base, layout, true};
+        return attention(kv, q, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, &f);
+    }
+    // vector-ALU plans, context-parallel shards on the decode kernel and
+    // splits of more blocks than one piece: the two kernels in a row; `out`
+    // holds the rotated queries when the caller wants none back (each output
+    // row is written only after its query row has been read)
     float* qr = q_rot ? q_rot : out;
     st = rope_append(kv, q, k, v, qr, rope_base, layout, stream);
     if (st != KVD_OK) return st;

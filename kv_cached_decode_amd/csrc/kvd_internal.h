@@ -53,6 +53,7 @@ struct RopeAppendArgs {
     CacheView c;
     int32_t kv_bf16;
     int32_t interleaved;
+    int32_t skip_q;         // rotate and append the new K/V rows only (q and q_rot unused)
     RopeTheta theta;
     const float* q;
     const float* k;
@@ -76,10 +77,15 @@ struct AttnArgs {
     float* part_o;          // [B][T][Hq][S][D]   unnormalised partial outputs
     float* part_ml;         // [B][T][Hq][S][2]   (running max in log2 units, sum)
     float* lse;             // [B][T][Hq] natural-log log-sum-exp of the row, or null
-    // Fused decode step (matrix-core kernel only): q holds the raw queries;
-    // the kernel rotates them, appends the new K/V rows of its split to the
-    // cache and writes the rotated queries to q_rot when that is non-null.
+    // Fused decode step (matrix-core decode kernel only): q holds the raw
+    // queries; the kernel rotates them, appends the new K/V rows of its split
+    // to the cache and writes the rotated queries to q_rot when that is
+    // non-null.
     int32_t fused;
+    // Prefill kernel: q holds the raw queries, which the kernel rotates at
+    // their positions (the new K/V rows are appended by the RoPE/append
+    // kernel before it); the rotated queries go to q_rot when non-null.
+    int32_t rope_q;
     int32_t interleaved;
     RopeTheta theta;
     const float* k_new;     // [B][T][Hkv][D] new keys before RoPE
@@ -90,15 +96,16 @@ struct AttnArgs {
 // A split that holds no key of its sequence leaves, for its rows, a partial
 // that drops out of the merge (running max -1e30, sum 0, output 0), so the
 // merge combines every split without reading the sequence lengths.  With a
-// single split (a context-parallel shard without a key of the sequence, or
-// rows of padding tokens past a ragged chunk) the rows are final: output 0,
-// lse -inf.
+// single split (a context-parallel shard without a key of the sequence) the
+// rows are final: output 0, lse -inf.  Rows of padding tokens past a ragged
+// chunk are left as they are.
 __device__ inline void write_empty_partials(const AttnArgs& a, int b, int kvh, int split, int row0,
                                             int nrows) {
     const CacheView& c = a.c;
     const int D = c.D;
     const int lq = __builtin_ctz(D) - 2;      // D / 4 float4s a row (D a power of two >= 16)
-    const int n4 = (min(row0 + nrows, a.rows) - row0) << lq;
+    const int live = a.num_splits == 1 ? min(a.rows, n_new(c, b) * c.g) : a.rows;
+    const int n4 = max(0, min(row0 + nrows, live) - row0) << lq;
     const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int idx = threadIdx.x; idx < n4; idx += blockDim.x) {
         const int r = row0 + (idx >> lq), e4 = idx & ((1 << lq) - 1);

@@ -14,7 +14,8 @@
 // (B*T*(Hq + 2*Hkv)*D elements) and is latency-bound; a prefill chunk moves
 // tens of MB, so a thread takes four pairs of a head with two 16-byte loads
 // and stores, all its loads issued first.  Padding tokens of ragged chunks do
-// nothing.
+// nothing.  With skip_q only the K/V heads are taken (the attention kernel
+// then rotates the queries itself).
 #include "bf16_round.h"
 #include "kvd_internal.h"
 #include "rope_math.h"
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a, int 
     const int heads = c.Hq + 2 * c.Hkv;
     const int offa = a.interleaved ? 8 * k : 4 * k;
     const int offb = a.interleaved ? 8 * k + 4 : half + 4 * k;
-    const int h0 = blockIdx.y * rounds * slots + slot;
+    const int h0 = (a.skip_q ? c.Hq : 0) + blockIdx.y * rounds * slots + slot;
 
     // This thread's inputs first (they do not depend on the angles), so their
     // latency overlaps the fp64 angle evaluation below.
@@ -174,7 +175,7 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
     const int tokens = a.c.B * a.c.T;
     if (tokens == 0) return hipSuccess;
     const int slots = 256 / (a.c.D / 8);
-    const int heads = a.c.Hq + 2 * a.c.Hkv;
+    const int heads = (a.skip_q ? 0 : a.c.Hq) + 2 * a.c.Hkv;
     const int total = (heads + slots - 1) / slots;            // rounds of heads a token
     // few tokens: one round a workgroup (more workgroups); many: up to
     // MAX_ROUNDS, so that every workgroup keeps more loads in flight

@@ -95,9 +95,7 @@ def test_shards_merge_to_whole_cache(name, P, window, kernel):
 def test_prefill_shards_merge_to_whole_cache(window):
     """A chunk of 40 new tokens per sequence (160 query rows per kv head: the
     prefill kernel) cut into 3 shards, the same checks."""
-    spec = workloads.Spec("cp_prefill", 3, 40, 32, 8, 128, 16, "bf16", (100, 500), 10000.0, "normal",
-                          "shuffled", spare_frac=0.1, seed=83)
-    check_shards(spec, 3, window, kb.KVD_KERNEL_AUTO)
+    check_shards(CP_PREFILL, 3, window, kb.KVD_KERNEL_AUTO)
 
 
 def check_shards(spec, P, window, kernel):
@@ -184,16 +182,23 @@ def test_merge_of_many_parts(P):
     assert np.max(np.abs(mlse[live] - (M + np.log(np.where(S > 0, S, 1.0)))[live])) <= 1e-5
 
 
-@pytest.mark.parametrize("name,kernel", [("mtp_verify", kb.KVD_KERNEL_AUTO), ("llama3_8b", kb.KVD_KERNEL_VALU)])
-def test_every_shard_runs_the_whole_step(name, kernel):
+CP_PREFILL = workloads.Spec("cp_prefill", 3, 40, 32, 8, 128, 16, "bf16", (100, 500), 10000.0, "normal",
+                            "shuffled", spare_frac=0.1, seed=83)
+
+
+@pytest.mark.parametrize("sp,kernel", [(workloads.small_variant("mtp_verify"), kb.KVD_KERNEL_AUTO),
+                                       (workloads.small_variant("llama3_8b"), kb.KVD_KERNEL_VALU),
+                                       (CP_PREFILL, kb.KVD_KERNEL_AUTO)],
+                         ids=["mtp_verify", "llama3_8b-valu", "prefill"])
+def test_every_shard_runs_the_whole_step(sp, kernel):
     """Each shard calls kvd_decode_step with the same new tokens, as every GPU
     of a context-parallel group would: the shards that do not hold the new
     tokens rotate the queries and store nothing, the tail shard appends, so
     the pools end exactly as the oracle's whole-cache append leaves them, and
     each shard's output is its partial over the keys it holds."""
-    spec = workloads.small_variant(name)
+    spec = sp
     w = cached_workload(spec)
-    note("every shard steps", name, kernel)
+    note("every shard steps", spec.name, kernel)
     case = GpuCase(w)
     P = 3
     cuts = shard_cuts(w, P, seed=11)

@@ -175,3 +175,72 @@ def test_v_outside_fp16_range(factor, every, splits):
     _, ref, kp_ref, vp_ref = oracle_step(w)
     assert np.array_equal(vp, vp_ref)
     assert_parity(sp, out, ref)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def _step_vs_two_calls(w, window=0, splits=0, want_q_rot=True):
+    """kvd_decode_step on a prefill plan (the RoPE/append kernel for the new
+    K/V rows, then the prefill kernel rotating its own queries) against the
+    two calls with the same plan: every real row bitwise, both pools bitwise,
+    and the padding rows of out and q_rot left as they were (NaN sentinels).
+    Returns (out, q_rot) of the step."""
+    s = w.spec
+    ref_case, case = GpuCase(w, window=window), GpuCase(w, window=window)
+    assert kb.decode_attention_plan(case.kv, num_splits=splits)[2] == kb.KVD_KERNEL_MFMA
+    q_rot_ref = torch.full_like(ref_case.q, float("nan"))
+    kb.rope_append_kv(ref_case.kv, ref_case.q, ref_case.k, ref_case.v, q_rot_ref, s.rope_base, s.layout)
+    out_ref = kb.decode_attention(ref_case.kv, q_rot_ref, torch.full_like(ref_case.q, float("nan")),
+                                  num_splits=splits)
+    out = torch.full_like(case.q, float("nan"))
+    q_rot = torch.full_like(case.q, float("nan")) if want_q_rot else None
+    kb.decode_step(case.kv, case.q, case.k, case.v, out=out, q_rot=q_rot, rope_base=s.rope_base,
+                   layout=s.layout, num_splits=splits)
+    torch.cuda.synchronize()
+    out, out_ref = out.cpu().numpy(), out_ref.cpu().numpy()
+    q_lens = w.q_lens if w.q_lens is not None else np.full(s.num_seqs, s.q_tokens)
+    real = np.arange(s.q_tokens)[None, :] < q_lens[:, None]            # [B][T]
+    assert np.array_equal(_bits(out[real]), _bits(out_ref[real])), "step differs from the two calls"
+    assert np.all(np.isnan(out[~real])), "padding rows of out were written"
+    for a_, b_ in zip(ref_case.pools(), case.pools()):
+        assert np.array_equal(a_, b_), "pools differ"
+    if want_q_rot:
+        q_rot, q_rot_ref = q_rot.cpu().numpy(), q_rot_ref.cpu().numpy()
+        assert np.array_equal(_bits(q_rot[real]), _bits(q_rot_ref[real])), "q_rot differs"
+        assert np.all(np.isnan(q_rot[~real])), "padding rows of q_rot were written"
+    return out, q_rot, case
+
+
+STEP_CASES = CASES + [
+    spec("ragged_g2", 3, 90, 16, 8, (0, 500), 73, chunk=(1, 90)),     # g = 2: 180 rows, 64 tokens a tile
+    spec("mha_long", 2, 200, 8, 8, (0, 300), 74, chunk=(150, 200)),   # g = 1: 128 tokens a tile
+]
+
+
+@pytest.mark.parametrize("sp", STEP_CASES, ids=lambda s: s.name)
+@pytest.mark.parametrize("want_q_rot", [True, False], ids=["q_rot", "no_q_rot"])
+def test_prefill_step_rotates_its_own_queries(sp, want_q_rot):
+    w = workloads.make_workload(sp)
+    note("prefill step", sp.name, want_q_rot)
+    out, q_rot, case = _step_vs_two_calls(w, want_q_rot=want_q_rot)
+    q_ref, ref, kp_ref, vp_ref = oracle_step(w)
+    kp, vp = case.pools()
+    assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref)
+    q_lens = w.q_lens if w.q_lens is not None else np.full(sp.num_seqs, sp.q_tokens)
+    real = np.arange(sp.q_tokens)[None, :] < q_lens[:, None]
+    if want_q_rot:
+        assert_qrot(q_rot[real], q_ref[real])
+    assert_parity(sp, out[real], ref[real], label=f"prefill_step/{sp.name}")
+
+
+@pytest.mark.parametrize("layout,window,splits", [(1, 0, 0), (0, 37, 0), (1, 100, 3), (0, 0, 3)])
+def test_prefill_step_layouts_windows_splits(layout, window, splits):
+    sp = spec("prefill_step_var", 3, 80, 32, 8, (0, 400), 75, chunk=(10, 80)).with_(layout=layout)
+    w = workloads.make_workload(sp)
+    note("prefill step variants", layout, window, splits)
+    out, _, _ = _step_vs_two_calls(w, window=window, splits=splits)
+    _, ref, _, _ = oracle_step(w, window=window)
+    real = np.arange(sp.q_tokens)[None, :] < w.q_lens[:, None]
+    assert_parity(sp, out[real], ref[real])
