@@ -15,7 +15,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvd.so")
+# the library built next to this file; KVD_LIB_PATH names another build of it
+# (the host-sanitizer build the CPU tests load)
+LIB_PATH = os.environ.get("KVD_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libkvd.so")
 
 KVD_OK, KVD_ERR_NULL, KVD_ERR_SHAPE, KVD_ERR_UNSUPPORTED, KVD_ERR_WORKSPACE, KVD_ERR_LAUNCH = range(6)
 KVD_KV_F32, KVD_KV_BF16 = 0, 1

@@ -28,10 +28,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+# Host code only (the device code is never instrumented): AddressSanitizer
+# and UndefinedBehaviorSanitizer with the shared ASan runtime, which a
+# process preloads to load the library.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-shared-libasan", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src, verbose, build_dir, extra):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC] + lang + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + lang + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,19 +47,24 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize_host: bool = False, out: str = None) -> str:
+    """Compile libkvd.so into `out` (default next to this file); with
+    `sanitize_host`, the host code is instrumented (a separate build folder)."""
+    lib = out or LIB
+    extra = SANITIZE_HOST if sanitize_host else []
+    build_dir = BUILD_DIR + ("_sanitize" if sanitize_host else "")
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + extra + ["-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libkvd.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -40,7 +40,8 @@ class _Cache(ctypes.Structure):
 
 
 _lib = None
-_lib_path = LIB
+# KVD_ORACLE_LIB names another build of kvd_oracle.c (the sanitizer build)
+_lib_path = os.environ.get("KVD_ORACLE_LIB") or LIB
 
 
 def use_library(path=None):

@@ -11,16 +11,24 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libkvd_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+# AddressSanitizer and UndefinedBehaviorSanitizer, every finding fatal
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = None) -> str:
+    """Compile kvd_oracle.c into `out` (default oracle/libkvd_oracle.so);
+    with `sanitize`, instrumented for ASan and UBSan (load it with gcc's
+    libasan preloaded)."""
     src = os.path.join(HERE, "kvd_oracle.c")
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    lib = out or LIB
+    tmp = lib + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O1" if sanitize else "-O2", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra"] + (SANITIZE if sanitize else []) + ["-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
