@@ -19,8 +19,11 @@
  *     memory on the current device) unless a comment says otherwise; the
  *     descriptor itself lives in host memory and is read during the call only.
  *   - The caller owns every buffer.  The library never allocates, frees or
- *     synchronises, and keeps no state between calls except a per-thread error
- *     string and a per-device cache of the compute-unit count.
+ *     synchronises, and keeps no state between calls except caches that
+ *     change no result: a per-thread error string, a per-thread copy of the
+ *     last RoPE frequency table (theta_i for the last base and head_dim), a
+ *     per-device cache of the compute-unit count and, for
+ *     kvd_decode_step_noalloc, the per-device address of its static scratch.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  It launches kernels and returns.
  *   - Arguments are validated on the host first.  On any error nothing is
@@ -171,15 +174,24 @@ typedef struct kvd_attn_options {
     int32_t kernel;
 } kvd_attn_options;
 
+/* The counter region at the head of every split-K workspace (see
+ * kvd_decode_attention); batches of more than 4096 (sequence, kv head) pairs
+ * merge their splits in a second kernel instead. */
+#define KVD_WORKSPACE_COUNTER_BYTES ((size_t)16384)
+
 /* Bytes of device workspace kvd_decode_attention needs for this descriptor on
  * the current device (0 when no split-K partials are needed).  Returns
- * (size_t)-1 for an invalid descriptor. */
+ * (size_t)-1 for an invalid descriptor.  The Ferrum Infer README ("Key
+ * Optimizations") names split-K flash decoding for long caches; the pages
+ * show no interface for its scratch, so the caller owns it, sized here. */
 size_t kvd_decode_attention_workspace_size(const kvd_paged_kv *kv);
 size_t kvd_decode_attention_workspace_size_ex(const kvd_paged_kv *kv,
                                               const kvd_attn_options *opt);
 
 /* The plan kvd_decode_attention would use: key-range partitions per (seq, kv
- * head), keys per partition and kernel family.  Any out pointer may be NULL. */
+ * head), keys per partition and kernel family.  Any out pointer may be NULL.
+ * The pages define no such call (the Ferrum Infer README only says split-K
+ * switches on for long caches); it reports this library's choice. */
 int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options *opt,
                                   int32_t *num_splits, int32_t *keys_per_split,
                                   int32_t *kernel);
@@ -197,12 +209,19 @@ int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options
  *   softmax_scale  scale; 0 means 1/sqrt(D).
  *   workspace      device scratch of at least kvd_decode_attention_workspace_size
  *                  bytes (may be NULL when that is 0), 256-byte aligned.  Its
- *                  contents need no initialisation and are clobbered; calls
+ *                  first KVD_WORKSPACE_COUNTER_BYTES hold arrival counters
+ *                  (with several splits the last workgroup of each (sequence,
+ *                  kv head) to finish merges the splits itself): they must
+ *                  be zero before a workspace is first used -- allocate it
+ *                  zeroed -- and every call leaves them zero again, so one
+ *                  workspace serves calls of any shape, eager or replayed
+ *                  in a HIP graph.  The rest is clobbered scratch.  Calls
  *                  that share a workspace must not run concurrently.
  *
  * Accumulation is fp32; the cache is read in kv_dtype.  Cache slots past
  * seq_lens (tail slots, unused blocks) are never read, whatever they hold.
- * For a fixed plan the result is bitwise deterministic (no atomics).
+ * For a fixed plan the result is bitwise deterministic: the splits are
+ * merged in a fixed order whichever finishes last.
  *
  * Arithmetic.  fp32 caches, and bf16 caches on the vector-ALU kernel: fp32
  * vector arithmetic on the cached values.  bf16 caches on the matrix cores
@@ -296,10 +315,12 @@ int32_t kvd_decode_step(const kvd_paged_kv *kv, const float *q, const float *k, 
  *   KVD_ERR_WORKSPACE and enqueues nothing.  A plan with several splits
  *   takes (head_dim + 2) * 4 bytes per (query row, split) pair, so 8 MiB
  *   holds about 16000 pairs at head_dim 128; plans of one split need none.
- *   Every call on one GPU shares that GPU's array, and each call rewrites
- *   every partial it reads (nothing needs clearing between calls), so calls
- *   that may overlap on one GPU -- on different streams, or from different
- *   host threads without ordering -- race and must not be issued.
+ *   Every call on one GPU shares that GPU's array (zero when the library is
+ *   loaded; every call rewrites the partials it reads and leaves the
+ *   arrival counters at its head zero, so nothing needs clearing between
+ *   calls), so calls that may overlap on one GPU -- on different streams,
+ *   or from different host threads without ordering -- race and must not be
+ *   issued.
  *   The first call on a device looks the array's address up (a runtime query,
  *   no allocation); a failure there returns KVD_ERR_LAUNCH.
  */
@@ -309,7 +330,41 @@ int32_t kvd_decode_step_noalloc(const kvd_paged_kv *kv, const float *q, const fl
                                 int32_t layout, float softmax_scale, const kvd_attn_options *opt,
                                 void *stream);
 
-/* Human-readable name of a status code (static storage). */
+/*
+ * Optional debug check of the descriptor's device-side contract: the parts
+ * that live in device memory and that the entry points above take on trust
+ * (their violation is undefined behaviour there).  The pages report such
+ * errors as values (ferric-core generate.rs returns Result and asserts its
+ * shapes); a caller that cannot vouch for its batch runs this check on the
+ * same stream before the step and reads the flag word.
+ *
+ *   flags  device pointer to one 32-bit word (4-byte aligned).  The kernel
+ *          ORs in a KVD_CHECK_* bit for every kind of violation it finds and
+ *          leaves the word as it was otherwise, so the caller clears it
+ *          first (or keeps accumulating over calls).
+ *     KVD_CHECK_SEQ_LEN   a seq_lens[b] below 0 or above max_seq_len, or,
+ *                         for a whole cache, below the sequence's new tokens
+ *     KVD_CHECK_BLOCK_ID  a block-table entry for a key some query sees
+ *                         (from the first query's window on) outside
+ *                         [0, num_blocks)
+ *     KVD_CHECK_Q_LENS    a q_lens[b] below 0 or above q_tokens_per_seq
+ *     KVD_CHECK_SHARD     a negative key_pos0[b] or q_pos[b]
+ * Host-side validation as for the other calls first.  One workgroup per
+ * sequence; it reads seq_lens, q_lens, key_pos0, q_pos and the table rows
+ * (never past a row) and dereferences no block id, so it is safe on any
+ * descriptor the host validation accepts.  Asynchronous on `stream`.
+ */
+enum {
+    KVD_CHECK_SEQ_LEN = 1,
+    KVD_CHECK_BLOCK_ID = 2,
+    KVD_CHECK_Q_LENS = 4,
+    KVD_CHECK_SHARD = 8
+};
+int32_t kvd_check_descriptor(const kvd_paged_kv *kv, uint32_t *flags, void *stream);
+
+/* Human-readable name of a status code (static storage).  The error calls
+ * stand for the pages' errors as values (generate.rs: Result, unwrap); the
+ * pages define no C form of them. */
 const char *kvd_status_string(int32_t status);
 
 /* Detail of the last non-OK status returned on the calling thread (static or

@@ -30,11 +30,14 @@ EXPORTED = [
     "kvd_decode_attention_workspace_size", "kvd_decode_attention_workspace_size_ex",
     "kvd_decode_attention_plan", "kvd_decode_step", "kvd_decode_step_noalloc",
     "kvd_decode_attention_lse", "kvd_merge_partials", "kvd_status_string", "kvd_last_error",
-    "kvd_abi_version", "kvd_probe_stream_read",
+    "kvd_abi_version", "kvd_probe_stream_read", "kvd_check_descriptor",
 ]
+KVD_CHECK_SEQ_LEN, KVD_CHECK_BLOCK_ID, KVD_CHECK_Q_LENS, KVD_CHECK_SHARD = 1, 2, 4, 8
 
 # bytes of the per-device static scratch of kvd_decode_step_noalloc (kvd.h)
 NOALLOC_SCRATCH_BYTES = 8 << 20
+# the arrival counters at the head of every split-K workspace (kvd.h)
+WORKSPACE_COUNTER_BYTES = 16384
 
 
 class KvdPagedKV(ctypes.Structure):
@@ -112,6 +115,8 @@ def lib():
         L.kvd_last_error.argtypes = []
         L.kvd_last_error.restype = ctypes.c_char_p
         L.kvd_abi_version.restype = I32
+        L.kvd_check_descriptor.argtypes = [KV, P, P]
+        L.kvd_check_descriptor.restype = I32
         L.kvd_probe_stream_read.argtypes = [P, SZ, I32, I32, I32, P, P]
         L.kvd_probe_stream_read.restype = I32
         _lib = L
@@ -283,8 +288,9 @@ def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO, stream=None):
     is needed), one per (device, stream): calls that share a workspace must
     not run concurrently, so work on different streams gets different
     buffers.  The buffer is allocated on that stream (torch's allocator then
-    reuses a replaced one only for work ordered after it there).  Allocation
-    happens here, outside the library; the contents need no initialisation."""
+    reuses a replaced one only for work ordered after it there), zeroed once
+    (its head holds arrival counters that every call leaves at zero).
+    Allocation happens here, outside the library."""
     n = decode_attention_workspace_size(kv, num_splits, kernel)
     if n == 0:
         return None
@@ -295,7 +301,7 @@ def workspace(kv: PagedKV, num_splits=0, kernel=KVD_KERNEL_AUTO, stream=None):
     if buf is None or buf.numel() < n:
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         with torch.cuda.stream(s) if isinstance(s, torch.cuda.Stream) else _nullcontext():
-            buf = torch.empty(n, dtype=torch.uint8, device=dev)
+            buf = torch.zeros(n, dtype=torch.uint8, device=dev)   # the arrival counters start at zero
         _ws_cache[key] = buf
     return buf
 
@@ -425,6 +431,19 @@ def merge_partials(outs, lses, out=None, lse_out=None, stream=None):
                                     lse_out.data_ptr(), _stream_handle(stream)),
            "kvd_merge_partials")
     return out, lse_out
+
+
+def check_descriptor(kv: PagedKV, flags=None, stream=None):
+    """kvd_check_descriptor: the descriptor's device-side contract checked on
+    the GPU; returns the flag word (a 1-element int32 device tensor, cleared
+    here when allocated here) with KVD_CHECK_* bits for the violations."""
+    if flags is None:
+        flags = torch.zeros(1, dtype=torch.int32, device=kv.seq_lens.device)
+    _need(flags, "flags", torch.int32, (1,))
+    d = kv.struct()
+    _check(lib().kvd_check_descriptor(ctypes.byref(d), flags.data_ptr(), _stream_handle(stream)),
+           "kvd_check_descriptor")
+    return flags
 
 
 def probe_stream_read(buf, workgroups, threads=256, unroll=4, sink=None, stream=None):

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kvd.cpp", "rope_append.hip", "attn_valu.hip", "attn_mfma.hip", "attn_prefill.hip",
-           "attn_combine.hip", "stream_probe.hip"]
+           "attn_combine.hip", "stream_probe.hip", "check_descriptor.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -182,6 +182,89 @@ __device__ inline int lpt_unit_pick(const AttnArgs& a, int pos, unsigned* sm_key
     return u;
 }
 
+constexpr int PER_THREAD = 16 * D / 256;     // (row, dim) elements of a workgroup's 16 rows per thread
+
+// The end of a split when the kernel merges its own splits.  Once every
+// thread's partial stores have completed (agent scope, so visible to every
+// workgroup from then on; an empty split stores nothing), one ticket per
+// workgroup.  The workgroup that takes the last ticket of its (sequence, kv
+// head) resets the counter for the next call and merges the splits with the
+// combine kernel's formula and order (split 0 first): its own split from
+// registers, a split that holds no key of the sequence as the neutral
+// partial (running max M_EMPTY, sum 0, output 0), the others read back with
+// agent-scope loads -- so the result does not depend on which split finished
+// last.  Rows of padding tokens are left as they are.
+__device__ __forceinline__ void merge_own_splits(const AttnArgs& a, int b, int kvh, int split, int nn, int first_key,
+                                 int rend, const float (&own_o)[PER_THREAD], const float (&own_m)[PER_THREAD],
+                                 const float (&own_l)[PER_THREAD]) {
+    const CacheView& c = a.c;
+    __shared__ unsigned sm_ticket;
+    __builtin_amdgcn_s_waitcnt(0);          // every counter at zero: this thread's stores are done
+    __syncthreads();
+    unsigned* const cnt = a.counters + (size_t)b * c.Hkv + kvh;
+    if (threadIdx.x == 0) sm_ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int S = a.num_splits;
+    if (sm_ticket != (unsigned)(S - 1)) return;
+    if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // splits s >= live hold no key of the sequence
+    const int live = rend > first_key ? min(S, (rend - first_key + a.split_keys - 1) / a.split_keys) : 0;
+    constexpr int MAXS = 8;                 // up to this many splits, every load goes out at once
+#pragma unroll
+    for (int k = 0; k < PER_THREAD; ++k) {
+        const int idx = (int)threadIdx.x + 256 * k;
+        const int r = idx / D, d = idx - r * D;
+        if (r >= a.rows) break;
+        const int t = r / c.g;
+        if (t >= nn) break;                 // padding rows (past a ragged chunk) are left as they are
+        const size_t qrow = ((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g);
+        const float* ml = a.part_ml + qrow * S * 2;
+        const float* po = a.part_o + qrow * S * D + d;
+        auto load = [&](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        float M = -INFINITY, Ls = 0.0f, O = 0.0f;
+        if (S <= MAXS) {
+            float ms[MAXS], ls[MAXS], os[MAXS];
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s) {
+                ms[s] = M_EMPTY;
+                ls[s] = os[s] = 0.0f;
+                if (s >= S) continue;
+                if (s == split) {
+                    ms[s] = own_m[k];
+                    ls[s] = own_l[k];
+                    os[s] = own_o[k];
+                } else if (s < live) {
+                    ms[s] = load(ml + 2 * s);
+                    ls[s] = load(ml + 2 * s + 1);
+                    os[s] = load(po + (size_t)s * D);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s)
+                if (s < S) M = fmaxf(M, ms[s]);
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s)
+                if (s < S) {
+                    const float f = exp2f(ms[s] - M);
+                    Ls += ls[s] * f;
+                    O += os[s] * f;
+                }
+        } else {
+            auto m_of = [&](int s) { return s == split ? own_m[k] : s < live ? load(ml + 2 * s) : M_EMPTY; };
+            for (int s = 0; s < S; ++s) M = fmaxf(M, m_of(s));
+            for (int s = 0; s < S; ++s) {
+                const float f = exp2f(m_of(s) - M);
+                const float l = s == split ? own_l[k] : s < live ? load(ml + 2 * s + 1) : 0.0f;
+                const float o = s == split ? own_o[k] : s < live ? load(po + (size_t)s * D) : 0.0f;
+                Ls += l * f;
+                O += o * f;
+            }
+        }
+        a.out[qrow * D + d] = finish_out(O, Ls);
+        if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
+    }
+}
+
 template <bool FUSED>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // the V tiles during the key loop, then the per-wave outputs
@@ -324,8 +407,20 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     const int nn = n_new(c, b);          // new tokens of this sequence (rows past them: padding)
     const int key_begin = split_begin(qo);
     const int rend = range_end(c, L, qo, nn);
+    const bool self_merge = a.num_splits > 1 && a.counters;
     if (key_begin >= rend) {            // empty split
-        write_empty_partials(a, b, kvh, split, 0, a.rows);
+        if (self_merge) {
+            float own_o[PER_THREAD], own_m[PER_THREAD], own_l[PER_THREAD];
+#pragma unroll
+            for (int k = 0; k < PER_THREAD; ++k) {
+                own_o[k] = 0.0f;
+                own_m[k] = M_EMPTY;
+                own_l[k] = 0.0f;
+            }
+            merge_own_splits(a, b, kvh, split, nn, range_start(c, qo), rend, own_o, own_m, own_l);
+        } else {
+            write_empty_partials(a, b, kvh, split, 0, a.rows);
+        }
         return;
     }
     const int key_end = min(rend, key_begin + a.split_keys);
@@ -631,8 +726,14 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         for (int i = 0; i < 4; ++i) sm_o[wave][n16][16 * nt + 4 * j + i] = o[nt][i];
     __syncthreads();
 
-    // merge the four waves; write the rows (one split) or the partial
-    for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
+    // merge the four waves; write the rows (one split) or the partial.  With
+    // several splits and arrival counters, the partial is published with
+    // agent-scope stores (coherent across the XCDs without a cache
+    // write-back) and this thread keeps its values for a merge of its own.
+    float own_o[PER_THREAD], own_m[PER_THREAD], own_l[PER_THREAD];
+#pragma unroll
+    for (int k = 0; k < PER_THREAD; ++k) {
+        const int idx = (int)threadIdx.x + 256 * k;
         const int r = idx / D, d = idx - r * D;
         if (r >= a.rows) break;
         float M = sm_m[0][r];
@@ -652,6 +753,16 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             if (t >= nn) break;             // padding rows (past a ragged chunk) are left as they are
             a.out[qrow * D + d] = finish_out(O, Ls);
             if (a.lse && d == 0) a.lse[qrow] = finish_lse(M, Ls);
+        } else if (self_merge) {
+            const size_t part = qrow * a.num_splits + split;
+            __hip_atomic_store(a.part_o + part * D + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+                __hip_atomic_store(a.part_ml + part * 2 + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.part_ml + part * 2 + 1, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            own_o[k] = O;
+            own_m[k] = M;
+            own_l[k] = Ls;
         } else {
             a.part_o[(qrow * a.num_splits + split) * D + d] = O;
             if (d == 0) {
@@ -668,6 +779,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             const int r = idx / D, d = idx - r * D, t = r / c.g;
             if (t < nn) a.q_rot[(((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g)) * D + d] = sm_q[idx];
         }
+
+    if (self_merge) merge_own_splits(a, b, kvh, split, nn, range_start(c, qo), rend, own_o, own_m, own_l);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) { attn_mfma_body<false>(a); }

@@ -239,18 +239,27 @@ void partial_sizes(const kvd_paged_kv* kv, const Plan& p, size_t* n_o, size_t* n
     *n_ml = rows * 2;
 }
 
-// Workspace carve-up: [partial o | partial (m, l)], 256-byte aligned.
+// Workspace carve-up: [arrival counters | partial o | partial (m, l)], each
+// 256-byte aligned.  The counters take a fixed region at the head of every
+// split-K workspace, whatever the plan, so no call's partials ever land where
+// another call keeps its counters: a workspace zeroed once stays ready for
+// calls of any shape, since every call leaves the counters it used at zero.
+// They serve the matrix-core decode kernel, which merges its own splits when
+// the batch has at most COUNTER_SLOTS (sequence, kv head) pairs.
+constexpr size_t COUNTER_SLOTS = KVD_WORKSPACE_COUNTER_BYTES / sizeof(unsigned);
+
 struct Carve {
-    size_t o, ml, total;
+    size_t cnt, o, ml, total;
 };
 
 Carve carve(const kvd_paged_kv* kv, const Plan& p) {
-    Carve c{0, 0, 0};
+    Carve c{0, 0, 0, 0};
     size_t n_o, n_ml;
     partial_sizes(kv, p, &n_o, &n_ml);
     if (n_o == 0) return c;
-    c.o = 0;
-    c.ml = (n_o * sizeof(float) + 255) & ~size_t(255);
+    c.cnt = 0;
+    c.o = KVD_WORKSPACE_COUNTER_BYTES;
+    c.ml = c.o + ((n_o * sizeof(float) + 255) & ~size_t(255));
     c.total = c.ml + n_ml * sizeof(float);
     return c;
 }
@@ -357,6 +366,7 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
     a.out = out;
     a.part_o = nullptr;
     a.part_ml = nullptr;
+    a.counters = nullptr;
     a.lse = lse;
     a.fused = fuse != nullptr && !fuse->rope_q_only;
     a.rope_q = fuse != nullptr && fuse->rope_q_only;
@@ -369,13 +379,18 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
         const Carve cv = carve(kv, p);
         a.part_o = (float*)((char*)workspace + cv.o);
         a.part_ml = (float*)((char*)workspace + cv.ml);
+        // the decode kernel merges its own splits (the last workgroup of a
+        // (sequence, kv head) to finish); the other kernels leave partials
+        // for the combine kernel
+        if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && (size_t)kv->num_seqs * kv->n_kv_heads <= COUNTER_SLOTS)
+            a.counters = (unsigned*)((char*)workspace + cv.cnt);
     }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = p.prefill                     ? kvd::launch_attn_prefill(a, s)
                    : p.kernel == KVD_KERNEL_MFMA ? kvd::launch_attn_mfma(a, s)
                                                  : kvd::launch_attn_valu(a, s);
     if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "decode attention launch: %s", hipGetErrorString(e));
-    if (p.splits > 1) {
+    if (p.splits > 1 && !a.counters) {
         e = kvd::launch_attn_combine(a, s);
         if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "combine launch: %s", hipGetErrorString(e));
     }
@@ -474,6 +489,18 @@ int32_t kvd_decode_step(const kvd_paged_kv* kv, const float* q, const float* k, 
     st = rope_append(kv, q, k, v, qr, rope_base, layout, stream);
     if (st != KVD_OK) return st;
     return attention(kv, qr, out, nullptr, softmax_scale, opt, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t kvd_check_descriptor(const kvd_paged_kv* kv, uint32_t* flags, void* stream) {
+    int32_t st = check_desc(kv);
+    if (st != KVD_OK) return st;
+    if (!flags) return fail(KVD_ERR_NULL, "flags must be non-NULL");
+    if ((uintptr_t)flags & 3) return fail(KVD_ERR_SHAPE, "flags must be 4-byte aligned");
+    if (kv->num_seqs == 0) return ok();
+    hipError_t e = kvd::launch_check_descriptor(view_of(kv), kv->max_seq_len, kv->num_blocks, flags,
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVD_ERR_LAUNCH, "check launch: %s", hipGetErrorString(e));
+    return ok();
 }
 
 const char* kvd_status_string(int32_t s) {

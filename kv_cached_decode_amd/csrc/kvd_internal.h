@@ -77,6 +77,10 @@ struct AttnArgs {
     float* part_o;          // [B][T][Hq][S][D]   unnormalised partial outputs
     float* part_ml;         // [B][T][Hq][S][2]   (running max in log2 units, sum)
     float* lse;             // [B][T][Hq] natural-log log-sum-exp of the row, or null
+    // [B][Hkv] arrival counters (zero between calls), or null: with several
+    // splits, the last workgroup of a (sequence, kv head) to finish merges
+    // the partials itself instead of the combine kernel
+    unsigned* counters;
     // Fused decode step (matrix-core decode kernel only): q holds the raw
     // queries; the kernel rotates them, appends the new K/V rows of its split
     // to the cache and writes the rotated queries to q_rot when that is
@@ -127,6 +131,8 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t launch_check_descriptor(const CacheView& c, int max_seq_len, int num_blocks, unsigned* flags,
+                                   hipStream_t s);
 hipError_t launch_merge_partials(int n_parts, int64_t rows, int D, const float* outs, const float* lses,
                                  float* out, float* lse_out, hipStream_t s);
 

@@ -274,3 +274,17 @@ def test_noalloc_step_validates_before_anything_runs():
     assert need > kb.NOALLOC_SCRATCH_BYTES
     assert step(big, 20) == kb.KVD_ERR_WORKSPACE
     assert "static scratch" in kb.last_error()
+
+
+def test_check_descriptor_arguments():
+    """kvd_check_descriptor validates on the host like the other calls and
+    needs an aligned flag word; an empty batch launches nothing."""
+    L = kb.lib()
+    assert L.kvd_check_descriptor(None, FAKE, None) == kb.KVD_ERR_NULL
+    for kw, status in BAD:
+        assert L.kvd_check_descriptor(ctypes.byref(desc(**kw)), FAKE, None) == status, kw
+    d = desc(max_blocks_per_seq=64, max_seq_len=1000)
+    assert L.kvd_check_descriptor(ctypes.byref(d), None, None) == kb.KVD_ERR_NULL
+    assert L.kvd_check_descriptor(ctypes.byref(d), FAKE + 2, None) == kb.KVD_ERR_SHAPE
+    empty = desc(num_seqs=0, k_cache=0, v_cache=0, block_table=0, seq_lens=0)
+    assert L.kvd_check_descriptor(ctypes.byref(empty), FAKE, None) == kb.KVD_OK

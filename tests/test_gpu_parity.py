@@ -245,12 +245,16 @@ def test_each_kernel_family(name, kernel):
 
 @needs_gpu
 def test_one_workspace_across_shapes():
-    """One workspace, never cleared, serves calls of any shape and kernel;
-    repeated calls give identical results (it holds only scratch partials)."""
+    """One workspace, its counter head zeroed once and the rest garbage,
+    serves calls of any shape, split count and kernel in turn; repeated
+    calls give identical results (the counters return to zero after every
+    call and the partials are rewritten before they are read)."""
     ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")
+    ws[:kb.WORKSPACE_COUNTER_BYTES].zero_()
     cases = []
     for name, kernel, splits in [("llama3_8b", 2, 3), ("qwen3_0_6b_cb", 2, 4), ("llama3_8b", 1, 5),
-                                 ("mtp_verify", 2, 6), ("llama3_8b", 2, 3)]:
+                                 ("mtp_verify", 2, 6), ("llama3_8b", 2, 3), ("chunked_prefill", 2, 2),
+                                 ("qwen3_0_6b_cb", 2, 2)]:
         spec = workloads.small_variant(name)
         w = cached_workload(spec)
         case = GpuCase(w)

@@ -1,0 +1,82 @@
+"""GPU: the decode kernel's own merge of its splits.  With several splits,
+each workgroup publishes its partial with agent-scope stores and takes a
+ticket; the last of a (sequence, kv head) merges every split in a fixed
+order.  Consecutive calls run through one workspace with new queries each
+time (so every call's partials differ from the previous call's, and a stale
+read would show): each result equals the one-split result of the same
+queries (no merge there), lse included; repeated calls are bitwise equal;
+and the counters at the head of the workspace are zero after every call."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import DEV, GpuCase, cached_workload, note
+from kv_cached_decode_amd import binding as kb
+from kv_cached_decode_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _close(a, b, tol=2e-5):
+    return float((a - b).abs().max() / b.abs().max().clamp_min(1e-30)) <= tol
+
+
+@pytest.mark.parametrize("name,splits", [("llama3_8b", 2), ("llama3_8b", 5), ("qwen3_0_6b_cb", 3),
+                                         ("mtp_verify", 4), ("long_ctx", 8)])
+def test_merge_under_changing_queries(name, splits):
+    w = cached_workload(workloads.small_variant(name))
+    note("split merge", name, splits)
+    case = GpuCase(w)
+    kv = case.kv
+    assert kb.decode_attention_plan(kv, splits, kb.KVD_KERNEL_MFMA) [0] == splits
+    n = kb.decode_attention_workspace_size(kv, splits, kb.KVD_KERNEL_MFMA)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(splits)
+    for i in range(12):
+        q = torch.randn(kv.q_shape(), generator=g, device=DEV) * (1.0 + 3.0 * (i % 3))
+        out, lse = kb.decode_attention_lse(kv, q, workspace_buf=ws, num_splits=splits, kernel=kb.KVD_KERNEL_MFMA)
+        again = kb.decode_attention(kv, q, workspace_buf=ws, num_splits=splits, kernel=kb.KVD_KERNEL_MFMA)
+        one, lse1 = kb.decode_attention_lse(kv, q, num_splits=1, kernel=kb.KVD_KERNEL_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again), f"call {i}: not deterministic"
+        assert _close(out, one), f"call {i}: merged splits differ from one split"
+        assert torch.allclose(lse, lse1, rtol=1e-5, atol=1e-5), f"call {i}: lse differs"
+        assert not ws[:kb.WORKSPACE_COUNTER_BYTES].any(), f"call {i}: counters left nonzero"
+
+
+def test_merge_in_the_fused_step_through_graph_replays():
+    """The fused decode step at 3 splits captured in a HIP graph: every replay
+    (with eager calls and new queries in between) merges its splits afresh."""
+    spec = workloads.small_variant("llama3_8b")
+    w = cached_workload(spec)
+    note("split merge graph")
+    case = GpuCase(w)
+    n = kb.decode_attention_workspace_size(case.kv, 3)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(case.q)
+    q = case.q.clone()
+
+    def step():
+        kb.decode_step(case.kv, q, case.k, case.v, out=out, rope_base=spec.rope_base, workspace_buf=ws,
+                       num_splits=3)
+
+    step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    torch.cuda.synchronize()
+    g = torch.Generator(device=DEV).manual_seed(7)
+    for i in range(4):
+        q.copy_(torch.randn(q.shape, generator=g, device=DEV))
+        step()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager step"
+        assert not ws[:kb.WORKSPACE_COUNTER_BYTES].any()

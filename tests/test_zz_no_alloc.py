@@ -23,7 +23,7 @@ def bits(a):
 def with_workspace(case, splits):
     s = case.w.spec
     n = kb.decode_attention_workspace_size(case.kv, splits)
-    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=case.q.device)
+    ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=case.q.device)
     out, q_rot = torch.empty_like(case.q), torch.zeros_like(case.q)
     kb.decode_step(case.kv, case.q, case.k, case.v, out=out, q_rot=q_rot, rope_base=s.rope_base,
                    layout=s.layout, workspace_buf=ws, num_splits=splits)
