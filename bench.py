@@ -552,6 +552,26 @@ def summarize(prof_dir, workload, commands, record=True):
             out.append(f"| {k} | {h:.0f} | {m:.0f} | {h / max(h + m, 1.0):.1%} |")
         out.append("")
 
+    mix = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv_rows(os.path.join(prof_dir, "mix"), "counter_collection.csv"):
+        mix[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if mix:
+        out += ["## L2-to-memory read requests (--pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum "
+                "TCC_BUBBLE_sum TCC_EA0_RDREQ_DRAM_sum; per dispatch)", "",
+                "FETCH_SIZE counts TCC_BUBBLE requests as 128 bytes, TCC_EA0_RDREQ_32B as 32 and the rest "
+                "as 64; the calibration copy shows how a plain stream's requests fall.", "",
+                "| kernel | RDREQ | RDREQ_32B | BUBBLE | RDREQ_DRAM | MB if all RDREQ are 128 B |",
+                "|---|---|---|---|---|---|"]
+        for k in sorted(mix):
+            if not k.startswith(("attn_", "decode_step", "rope_append", "vectorized_elementwise")):
+                continue
+            m = {c: _median(v) for c, v in mix[k].items()}
+            rq = m.get("TCC_EA0_RDREQ_sum", 0.0)
+            out.append(f"| {k} | {rq:.0f} | {m.get('TCC_EA0_RDREQ_32B_sum', 0):.0f} | "
+                       f"{m.get('TCC_BUBBLE_sum', 0):.0f} | {m.get('TCC_EA0_RDREQ_DRAM_sum', 0):.0f} | "
+                       f"{rq * 128 / 1e6:.2f} |")
+        out.append("")
+
     util = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in _csv_rows(os.path.join(prof_dir, "util"), "counter_collection.csv"):
         util[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))

@@ -5,11 +5,12 @@
 // cache, head_dim 128.  Causal within the chunk: new token t sees the keys up
 // to its own position.
 //
-// Workgroup = 4 wave64s over a tile of 128 query rows of one (sequence, kv
-// head) -- wave w owns rows 32w .. 32w+31 of the tile as two 16-row blocks,
-// row r = t*g + hg -- and one key range (split).  Unlike the decode kernel,
-// every wave needs every key, so the K and V tiles (32 keys) are staged in
-// LDS once by all 256 threads and shared by the four waves: the kv-head
+// Workgroup = WAVES wave64s (4: two workgroups per CU) over a tile of 32 *
+// WAVES query rows of one (sequence, kv head) -- wave w owns rows 32w ..
+// 32w+31 of the tile as two 16-row blocks, row r = t*g + hg -- and one key
+// range (split).  Unlike the decode kernel, every wave needs every key, so
+// the K and V tiles (32 keys) are staged in LDS once by all the threads and
+// shared by the waves: the kv-head
 // group's rows share the keys, which is what makes the work dense enough for
 // the matrix cores.  Each K or V operand a wave reads from LDS feeds both of
 // its row blocks, so LDS reads per query row are half those of one block per
@@ -52,7 +53,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int WAVES = 4;
+constexpr int WAVES = PREFILL_WAVES;
+constexpr int THREADS = 64 * WAVES;
 constexpr int D = 128;
 constexpr int LOG2_ROW_BYTES = 8;         // one cached key or value row: D bf16
 static_assert((1 << LOG2_ROW_BYTES) == D * 2, "row bytes");
@@ -62,11 +64,14 @@ constexpr int WROWS = 16 * RB;            // query rows per wave
 constexpr int ROWS = WAVES * WROWS;       // query rows per workgroup
 constexpr int KROWB = D * 2 + 16;         // LDS row stride of the K tile: 16 rows read at one column hit distinct banks
 constexpr int VROWB = D * 2 + 32;         // LDS row stride of the V tile (transposed reads)
+constexpr int CHUNKS = TILE * D * 2 / 16;   // 16-byte chunks of a K (or V) tile
+constexpr int CPT = CHUNKS / THREADS;        // of them per thread
+static_assert(CPT * THREADS == CHUNKS, "the threads split a tile evenly");
 constexpr int K_BYTES = TILE * KROWB;
 constexpr int V_BYTES = TILE * VROWB;
 constexpr int MAX_STAGED_BLOCKS = 4096;   // block ids of a split, staged in LDS
 constexpr int RANK_MAX = PREFILL_RANK_MAX;  // units ranked longest-first (their key counts and the units by rank share the block-id array)
-static_assert(RANK_MAX <= 256, "one unit per thread in the ranking");
+static_assert(RANK_MAX <= THREADS, "one unit per thread in the ranking");
 constexpr float M_EMPTY = -1e30f;
 constexpr int HALF = D / 2;
 constexpr int ANG_TOKENS = 32;            // tokens whose angles share the LDS at a time
@@ -201,13 +206,13 @@ __device__ inline Unit unit_of(const AttnArgs& a, int u, int n_rtiles) {
 // order.  Any other head count, or fewer than 2*(32/m) units, keeps that
 // order throughout.  Only the balance depends on this.
 __device__ inline int cu_paired_rank(int pos, int n_units, int Hkv) {
-    if (Hkv % 8 != 0 || 32 % (Hkv / 8) != 0) return pos;
+    if (PREFILL_WGS_PER_CU != 2 || Hkv % 8 != 0 || 32 % (Hkv / 8) != 0) return pos;
     const int P = 32 / (Hkv / 8);
     if (pos < P || pos >= 2 * P || n_units < 2 * P) return pos;
     return 3 * P - 1 - pos;
 }
 
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kernel(AttnArgs a) {
     // the K and V tiles (double-buffered); before the first tile, the
     // cosines and sines of the query rotation
     __shared__ __attribute__((aligned(16))) char sm_kv[2 * K_BYTES + 2 * V_BYTES];
@@ -328,17 +333,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // Each thread moves 2 of the 512 16-byte chunks of a K tile and 2 of the
-    // V tile: chunk ch = tid + 256*i -> key ch / 16, column ch % 16.  Keys past
-    // the range re-read its last key (weight 0 below).
+    // Each thread moves CPT of the 512 16-byte chunks of a K tile and CPT of
+    // the V tile: chunk ch = tid + THREADS*i -> key ch / 16, column ch % 16.
+    // Keys past the range re-read its last key (weight 0 below).
     const char* kbase = (const char*)c.k;
     const char* vbase = (const char*)c.v;
     const int bs_mask = (1 << c.log2_bs) - 1;
-    u32x4 kr[2], vr[2];
+    u32x4 kr[CPT], vr[CPT];
     auto load = [&](int base) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ch = tid + 256 * i;
+        for (int i = 0; i < CPT; ++i) {
+            const int ch = tid + THREADS * i;
             const int key = min(base + (ch >> 4), key_end - 1);
             const unsigned hrow = sm_blk[(key >> c.log2_bs) - blk0];
             const size_t off = ((size_t)hrow << (c.log2_bs + LOG2_ROW_BYTES)) +
@@ -467,8 +472,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         unsigned vexp = 0u;             // the staged fp16 pairs, ORed (their exponent fields tell)
         auto stage = [&](int buf, bool f16) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ch = tid + 256 * i;
+            for (int i = 0; i < CPT; ++i) {
+                const int ch = tid + THREADS * i;
                 *(u32x4*)(sm_k[buf] + (ch >> 4) * KROWB + 16 * (ch & 15)) = kr[i];
                 u32x4 vs = vr[i];
                 if (f16) {
@@ -685,7 +690,7 @@ hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s) {
     const int64_t n = (int64_t)a.num_splits * n_rtiles * a.c.B * a.c.Hkv;
     if (n > INT32_MAX) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)n);
-    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(THREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -142,9 +142,9 @@ struct Plan {
 // Split-K plan from host-known sizes only (graph-capture safe).
 //
 // Kernel family: the matrix-core kernel when the g*T query rows sharing a kv
-// head reach MFMA_MIN_ROWS (bf16, head_dim 128), else the vector-ALU kernel.
-// The VALU path spends ~35 VALU instructions per cached key at 4 rows (about
-// 60% VALU-busy at 55-60% of HBM bandwidth); the matrix-core path ~14.
+// head reach MFMA_MIN_ROWS (bf16, head_dim 128: every such plan, the counters
+// behind it are given with the constant), else the vector-ALU kernel (fp32
+// caches, other head dims).
 //
 // Splits: long contiguous ranges stream best.  The matrix-core kernel runs
 // one workgroup per CU when the batch has fewer (sequence, kv head) units
@@ -161,7 +161,7 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     if (kernel != KVD_KERNEL_AUTO && kernel != KVD_KERNEL_VALU && kernel != KVD_KERNEL_MFMA)
         return fail(KVD_ERR_UNSUPPORTED, "kernel = %d", kernel);
     // the matrix-core kernels: the decode kernel up to 16 query rows per kv
-    // head, the prefill kernel (128-row tiles sharing LDS-staged K/V) beyond
+    // head, the prefill kernel (row tiles sharing LDS-staged K/V) beyond
     const bool mfma_ok = kvd::mfma_supported(D, bf16, 1);
     if (kernel == KVD_KERNEL_MFMA && !mfma_ok)
         return fail(KVD_ERR_UNSUPPORTED, "matrix-core kernels need a bf16 cache and head_dim 128");
@@ -185,7 +185,7 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
         p->row_tile = kvd::PREFILL_ROWS;
         n_rtiles = (int)cdiv(p->rows, kvd::PREFILL_ROWS);
         max_keys = (int64_t)4094 << log2_bs;
-        target = 2 * (int64_t)num_cus();
+        target = kvd::PREFILL_WGS_PER_CU * (int64_t)num_cus();
     } else if (kernel == KVD_KERNEL_MFMA) {
         step = kvd::mfma_step_keys();
         p->row_tile = 16;
@@ -357,7 +357,8 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
     // longest-first only pays when workgroups wait for a slot
     if (p.prefill) {
         const int64_t units = (int64_t)p.splits * cdiv(p.rows, kvd::PREFILL_ROWS) * kv->num_seqs;
-        a.rank_longest = units <= kvd::PREFILL_RANK_MAX && units * kv->n_kv_heads > 2 * (int64_t)num_cus();
+        a.rank_longest = units <= kvd::PREFILL_RANK_MAX &&
+                         units * kv->n_kv_heads > kvd::PREFILL_WGS_PER_CU * (int64_t)num_cus();
     } else {
         a.rank_longest = (int64_t)p.splits * kv->n_kv_heads * kv->num_seqs > (int64_t)kvd::MFMA_WGS_PER_CU * num_cus();
     }

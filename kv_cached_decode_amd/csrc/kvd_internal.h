@@ -151,8 +151,15 @@ int valu_max_row_tile(int D, int kv_bf16);   // rows one workgroup can hold
 constexpr int VALU_MAX_STAGED_BLOCKS = 4096;
 int valu_max_split_keys(int log2_bs);
 bool mfma_supported(int D, int kv_bf16, int rows);
+// Waves of one prefill workgroup (32 query rows each) and the workgroups a
+// CU holds at once (two waves per SIMD either way).  Four waves and two
+// workgroups per CU measured faster than eight and one (178 against 196 us
+// on the chunked prefill): a workgroup's waves wait at the per-tile barrier,
+// and a second workgroup on the CU fills those waits.
+constexpr int PREFILL_WAVES = 4;
+constexpr int PREFILL_WGS_PER_CU = PREFILL_WAVES == 4 ? 2 : 1;
 // Query rows of one prefill workgroup (more rows than the decode kernel takes).
-constexpr int PREFILL_ROWS = 128;
+constexpr int PREFILL_ROWS = 32 * PREFILL_WAVES;
 // Prefill grids of at most this many (sequence, row tile, split) units are
 // ordered longest-first inside the kernel.
 constexpr int PREFILL_RANK_MAX = 256;
@@ -163,8 +170,14 @@ constexpr int MFMA_WGS_PER_CU = 2;
 // Resident workgroups per CU for a kernel variant (occupancy query on the
 // current device; a conservative default when there is none).
 int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds);
-// Query rows (g*T) from which the matrix-core kernel is the default.
-constexpr int MFMA_MIN_ROWS = 2;
+// Query rows (g*T) from which the matrix-core kernel is the default: every
+// bf16 head_dim-128 plan.  Measured (rocprof, one layer's step): the
+// vector-ALU kernel reaches 57.6%, 60.6% and 35.5% of 8 TB/s at 4, 2 and 8
+// rows per kv head (64.5%, 39.6% and 65.3% VALU busy: issue-bound at 4 and 8
+// rows), the matrix-core kernel 72.2%, 72.5% and 81.4%; at one row per kv
+// head (multi-head attention) 76.7% against 78.2%, where the fused kernel
+// also saves the RoPE/append launch and the split combine.
+constexpr int MFMA_MIN_ROWS = 1;
 // Block ids the decode matrix-core kernel stages in LDS at a time (one
 // piece of a split).  The fused step needs a split's blocks in one piece:
 // its append takes the new keys' block ids from there.

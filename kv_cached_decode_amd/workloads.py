@@ -21,8 +21,8 @@ Workload shapes follow the five named configurations of the decode step:
 * ``chunked_prefill`` -- batch 8 of Llama-3-8B-shaped layers taking a prefill
   chunk each: ragged chunks of 64..512 new tokens (uniform per sequence) on
   ragged contexts uniform in [0, 4096], paged bf16 (block 16, shuffled).
-* ``llama2_7b_mha``  -- multi-head decode (one query head per kv head, the
-  case only the vector-ALU kernel serves): batch 16, 32 q = 32 kv heads,
+* ``llama2_7b_mha``  -- multi-head decode (one query row per kv head, where
+  the two kernel families come closest): batch 16, 32 q = 32 kv heads,
   head_dim 128, context 4096, paged bf16 (block 16, shuffled), values N(0,1).
 
 bf16 values are drawn as float32 and truncated to their top 16 bits (a

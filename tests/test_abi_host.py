@@ -195,10 +195,12 @@ def test_plan_covers_every_key(max_len, B, T, Hq, Hkv):
             assert ws >= rows * s * (128 + 2) * 4
 
 
-@pytest.mark.parametrize("B,T,Hq,Hkv", [(16, 1, 32, 8), (4, 1, 64, 8), (32, 4, 32, 8), (64, 1, 16, 8)])
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(16, 1, 32, 8), (4, 1, 64, 8), (32, 4, 32, 8), (64, 1, 16, 8),
+                                        (16, 1, 32, 32)])
 def test_matrix_core_plan(B, T, Hq, Hkv):
     """The matrix-core kernel covers every key with its splits and is the
-    automatic choice from 2 query rows per kv head."""
+    automatic choice for every bf16 cache of head_dim 128, one query row per
+    kv head included."""
     d = desc(num_seqs=B, q_tokens_per_seq=T, n_q_heads=Hq, n_kv_heads=Hkv, max_blocks_per_seq=1024,
              max_seq_len=16384)
     for forced in (0, 1, 3, 1000):
@@ -207,7 +209,7 @@ def test_matrix_core_plan(B, T, Hq, Hkv):
         if forced:
             assert s <= forced
     _, _, kern = _plan(d, 0, 0)
-    assert kern == (2 if (Hq // Hkv) * T >= 2 else 1)
+    assert kern == 2, "bf16, head_dim 128: the matrix cores, whatever the rows per kv head"
 
 
 def test_lse_and_merge_arguments():

@@ -53,13 +53,17 @@ def assert_same(a_case, b_case, a, b):
     assert np.array_equal(bits(va), bits(vb)), "V pool differs"
 
 
-# the four bf16 configurations (matrix-core plans, one fused kernel) and two
-# vector-ALU plans (the two kernels in a row): an fp32 cache, and a bf16
-# cache with one query row per kv head
+# the bf16 configurations (matrix-core plans: one fused kernel, or the
+# prefill kernel after the RoPE/append kernel) and vector-ALU plans (the two
+# kernels in a row): an fp32 cache, and a bf16 cache with one query row per
+# kv head with the kernel family forced (the automatic plan takes the matrix
+# cores there)
 SPECS = [workloads.small_variant(n) for n in workloads.CONFIG_ORDER[1:]] + [
     workloads.Spec("valu_f32", 3, 2, 8, 2, 64, 16, "f32", (600, 5000), 10000.0, "normal", "shuffled",
                    spare_frac=0.1, seed=77),
     workloads.Spec("valu_mha_bf16", 4, 1, 8, 8, 128, 16, "bf16", (100, 3000), 10000.0, "normal",
+                   "shuffled", spare_frac=0.1, seed=78),
+    workloads.Spec("mfma_mha_bf16", 4, 1, 8, 8, 128, 16, "bf16", (100, 3000), 10000.0, "normal",
                    "shuffled", spare_frac=0.1, seed=78),
     # matrix-core plans with more than 256 new-key pairs per kv head (the
     # append's later rounds): 16 tokens at g = 1, 8 tokens at g = 2
@@ -74,10 +78,11 @@ SPECS = [workloads.small_variant(n) for n in workloads.CONFIG_ORDER[1:]] + [
 @pytest.mark.parametrize("want_q_rot", [True, False], ids=["q_rot", "no_q_rot"])
 def test_fused_equals_two_calls_small(spec, want_q_rot):
     w = cached_workload(spec)
-    note("fused vs two calls", spec.name, want_q_rot)
+    kernel = kb.KVD_KERNEL_VALU if spec.name.startswith("valu") else kb.KVD_KERNEL_AUTO
+    note("fused vs two calls", spec.name, want_q_rot, kernel)
     ref_case, case = GpuCase(w), GpuCase(w)
-    ref = two_calls(ref_case)
-    got = fused(case, want_q_rot=want_q_rot)
+    ref = two_calls(ref_case, kernel=kernel)
+    got = fused(case, kernel=kernel, want_q_rot=want_q_rot)
     assert_same(ref_case, case, ref, got)
     _, out_ref, _, _ = oracle_step(w)
     assert_parity(spec, got[1], out_ref)
