@@ -528,7 +528,9 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
                         }
                     }
                 }
-                if (!whole) {
+                // (a branch, not selects: all but the last one or two tiles of
+                // a unit are whole for every row of the wave)
+                if (__builtin_expect(!whole, 0)) {
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
                     mx[rb] = x;
                 }
                 xor_max2(mx[0], mx[1]);
-                if (__builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1])) {
+                if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1]) != 0, 0)) {
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         const bool started = m[rb] != M_EMPTY;
@@ -610,7 +612,6 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
                         }
                     }
                 }
-
             }
             // the next tile into the other buffer (read two tiles ago, released
             // by the last barrier), then the one after it from HBM
