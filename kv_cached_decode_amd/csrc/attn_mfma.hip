@@ -551,25 +551,35 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     // K operands: tile h (16 keys), step kk: lane l reads key l%16, bytes
     // [64*kk + 16*j, +16).  V rows: load i reads key 4*i + j, chunk n16.
     // Keys past the piece end re-read its last key (weight 0 below).
-    // blk_of(key) gives the block id of a key of the tile.
+    // blk_of(key) gives the block id of a key of the tile.  V goes out
+    // before K: a tile first stores its V rows to LDS, which then waits for
+    // V alone (the memory counter is in order), and the next tile's V loads
+    // go out right after that store, before the tile's score MFMAs; the next
+    // K loads follow the MFMAs that free their registers.
     u32x4 kf[8], vf[8];
-    auto issue = [&](int base, int pend, auto&& blk_of) {
-        auto row = [&](const char* basep, int key) -> const char* {
-            const size_t slot = (((size_t)blk_of(key) * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
-            return basep + slot * (D * 2);
-        };
+    auto row_of = [&](const char* basep, int key, auto&& blk_of) -> const char* {
+        const size_t slot = (((size_t)blk_of(key) * c.Hkv + kvh) << c.log2_bs) + (key & bs_mask);
+        return basep + slot * (D * 2);
+    };
+    auto issue_v = [&](int base, int pend, auto&& blk_of) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const char* vr = row_of(vbase, min(base + 4 * i + j, pend - 1), blk_of);
+            vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
+        }
+    };
+    auto issue_k = [&](int base, int pend, auto&& blk_of) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const char* kr = row(kbase, min(base + 16 * h + n16, pend - 1));
+            const char* kr = row_of(kbase, min(base + 16 * h + n16, pend - 1), blk_of);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 kf[4 * h + kk] = __builtin_nontemporal_load((const u32x4*)(kr + 64 * kk + 16 * j));
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const char* vr = row(vbase, min(base + 4 * i + j, pend - 1));
-            vf[i] = __builtin_nontemporal_load((const u32x4*)(vr + 16 * n16));
-        }
+    };
+    auto issue = [&](int base, int pend, auto&& blk_of) {
+        issue_v(base, pend, blk_of);
+        issue_k(base, pend, blk_of);
     };
     const int first_p1 = (int)min((long long)key_end,
                                   ((long long)(key_begin >> c.log2_bs) + MAX_PIECE_BLOCKS) << c.log2_bs);
@@ -649,6 +659,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (4 * i + j) * ROWB + 16 * n16) = vf[i];
+            const bool more = base + STRIDE < p1;
+            if (more) issue_v(base + STRIDE, p1, staged);
 
             // scores: S^T tiles (16 keys x 16 rows), keys base + 16h + 4j + i
             f32x4 s[2];
@@ -663,7 +675,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
                 }
                 s[h] = acc;
             }
-            if (base + STRIDE < p1) issue(base + STRIDE, p1, staged);
+            if (more) issue_k(base + STRIDE, p1, staged);
 
             // mask, running max, weights
             float mx = m;
