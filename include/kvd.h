@@ -210,13 +210,15 @@ int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options
  *   workspace      device scratch of at least kvd_decode_attention_workspace_size
  *                  bytes (may be NULL when that is 0), 256-byte aligned.  Its
  *                  first KVD_WORKSPACE_COUNTER_BYTES hold arrival counters
- *                  (with several splits the last workgroup of each (sequence,
- *                  kv head) to finish merges the splits itself): they must
- *                  be zero before a workspace is first used -- allocate it
- *                  zeroed -- and every call leaves them zero again, so one
- *                  workspace serves calls of any shape, eager or replayed
- *                  in a HIP graph.  The rest is clobbered scratch.  Calls
- *                  that share a workspace must not run concurrently.
+ *                  (on a matrix-core decode plan of two splits the last
+ *                  workgroup of each (sequence, kv head) to finish merges
+ *                  the two itself; other plans merge in a second kernel):
+ *                  they must be zero before a workspace is first used --
+ *                  allocate it zeroed -- and every call leaves them zero
+ *                  again, so one workspace serves calls of any shape, eager
+ *                  or replayed in a HIP graph.  The rest is clobbered
+ *                  scratch.  Calls that share a workspace must not run
+ *                  concurrently.
  *
  * Accumulation is fp32; the cache is read in kv_dtype.  Cache slots past
  * seq_lens (tail slots, unused blocks) are never read, whatever they hold.

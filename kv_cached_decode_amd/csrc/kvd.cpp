@@ -380,10 +380,17 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
         const Carve cv = carve(kv, p);
         a.part_o = (float*)((char*)workspace + cv.o);
         a.part_ml = (float*)((char*)workspace + cv.ml);
-        // the decode kernel merges its own splits (the last workgroup of a
-        // (sequence, kv head) to finish); the other kernels leave partials
-        // for the combine kernel
-        if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && (size_t)kv->num_seqs * kv->n_kv_heads <= COUNTER_SLOTS)
+        // with two splits the decode kernel merges them itself (the last
+        // workgroup of a (sequence, kv head) to finish); otherwise the
+        // partials go to the combine kernel.  Measured (median step, same
+        // box, the two alternating): two splits, Llama-3-8B-shaped layer
+        // 47.6 -> 46.95 us with the merge in the kernel; three splits (the
+        // continuous batch) 173.4 against 174.2 us and eight (131k context)
+        // 323.9 against 326.2 us in favour of the combine kernel: the last
+        // workgroup's read-back of the other splits grows with their number
+        // and costs more than the second launch.
+        if (p.kernel == KVD_KERNEL_MFMA && !p.prefill && p.splits == kvd::SELF_MERGE_SPLITS &&
+            (size_t)kv->num_seqs * kv->n_kv_heads <= COUNTER_SLOTS)
             a.counters = (unsigned*)((char*)workspace + cv.cnt);
     }
     hipStream_t s = (hipStream_t)stream;

@@ -178,6 +178,9 @@ int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds);
 // head (multi-head attention) 76.7% against 78.2%, where the fused kernel
 // also saves the RoPE/append launch and the split combine.
 constexpr int MFMA_MIN_ROWS = 1;
+// Split count at which the decode matrix-core kernel merges its splits
+// itself instead of leaving them to the combine kernel.
+constexpr int SELF_MERGE_SPLITS = 2;
 // Block ids the decode matrix-core kernel stages in LDS at a time (one
 // piece of a split).  The fused step needs a split's blocks in one piece:
 // its append takes the new keys' block ids from there.
