@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import GpuCase, assert_parity, note, oracle_step
+from gpu_common import GpuCase, assert_parity, assert_qrot, note, oracle_step
 from kv_cached_decode_amd import binding as kb
 from kv_cached_decode_amd import workloads
 
@@ -30,23 +30,32 @@ def random_case(i):
     window = int(rng.choice([0, 0, 0, 7, 100]))
     spec = workloads.Spec(f"rand{i}", B, T, g * Hkv, Hkv, D, bs, dtype, ctx, 10000.0, "normal", "shuffled",
                           spare_frac=0.1, seed=2000 + i, layout=int(rng.integers(2)), chunk=chunk)
-    return spec, window
+    # drawn last, so the shapes above do not depend on them: a forced split
+    # count (two splits merge inside the decode kernel), and whether the
+    # rotated queries are asked for
+    splits = int(rng.choice([0, 0, 2, 3]))
+    want_q_rot = bool(rng.random() < 0.3)
+    return spec, window, splits, want_q_rot
 
 
-@pytest.mark.parametrize("i", range(48))
+@pytest.mark.parametrize("i", range(64))
 def test_random_shape(i):
-    spec, window = random_case(i)
+    spec, window, splits, want_q_rot = random_case(i)
     w = workloads.make_workload(spec)
-    note("random shape", i, spec, "window", window)
+    note("random shape", i, spec, "window", window, "splits", splits, "q_rot", want_q_rot)
     case = GpuCase(w, window=window)
-    out = kb.decode_step(case.kv, case.q, case.k, case.v, rope_base=spec.rope_base, layout=spec.layout)
+    res = kb.decode_step(case.kv, case.q, case.k, case.v, rope_base=spec.rope_base, layout=spec.layout,
+                         num_splits=splits, want_q_rot=want_q_rot)
     torch.cuda.synchronize()
-    out = out.cpu().numpy()
+    out = (res[0] if want_q_rot else res).cpu().numpy()
     kp, vp = case.pools()
-    _, ref, kp_ref, vp_ref = oracle_step(w, window=window)
+    q_ref, ref, kp_ref, vp_ref = oracle_step(w, window=window)
     assert np.array_equal(kp.view(np.uint8), kp_ref.view(np.uint8)), "K pool differs"
     assert np.array_equal(vp.view(np.uint8), vp_ref.view(np.uint8)), "V pool differs"
+    real = np.ones(out.shape[:2], bool)
     if w.q_lens is not None:
-        for b, n in enumerate(w.q_lens):
-            assert np.all(out[b, n:] == 0.0), "padding rows must be 0"
+        real = np.arange(spec.q_tokens)[None, :] < w.q_lens[:, None]
+        assert np.all(out[~real] == 0.0), "padding rows of a zeroed out must stay 0"
+    if want_q_rot:
+        assert_qrot(res[1].cpu().numpy()[real], q_ref[real])
     assert_parity(spec, out, ref)
