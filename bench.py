@@ -471,7 +471,8 @@ def _median(v):
 
 def summarize(prof_dir, workload, commands, record=True):
     """Turn rocprofv3 CSV output (kt/ kernel trace, fetch/ FETCH_SIZE,
-    write/ WRITE_SIZE, util/ utilisation counters, tcc/ L2 hits and misses)
+    write/ WRITE_SIZE, util/ utilisation counters, tcc/ L2 hits and misses,
+    mix/ request sizes, issue/ and insts/ issue, stall and instruction counts)
     into a markdown summary on stdout and, with `record` (runs of the
     automatic plan), record the calibrated traffic per call."""
     import collections
@@ -591,6 +592,42 @@ def summarize(prof_dir, workload, commands, record=True):
                        f"{m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / 1024 / cyc:.2%} | "
                        f"{m.get('SQ_INSTS_VALU', 0) / max(m.get('SQ_WAVES', 1), 1):.0f} | "
                        f"{m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+        out.append("")
+
+    # where the waves' time goes: issuing, waiting on a counter (s_waitcnt,
+    # barriers), or holding an instruction that cannot issue yet; and the
+    # instruction mix per wave
+    issue = collections.defaultdict(lambda: collections.defaultdict(list))
+    for sub in ("issue", "insts"):
+        for r in _csv_rows(os.path.join(prof_dir, sub), "counter_collection.csv"):
+            issue[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if issue:
+        out += ["## Issue and stalls (--pmc SQ_WAVE_CYCLES SQ_ACTIVE_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_ANY "
+                "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_MFMA, then "
+                "--pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 SQ_WAVES "
+                "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE)", "",
+                "Shares of the waves' lifetime (SQ_WAVE_CYCLES): issuing instructions (SQ_ACTIVE_INST_ANY), "
+                "waiting (SQ_WAIT_ANY: on s_waitcnt counters, barriers, dependencies) and waiting for an "
+                "instruction to issue (SQ_WAIT_INST_ANY). Co-execution: cycles with the matrix cores and "
+                "the vector ALU busy at once (SQ_VALU_MFMA_COEXEC_CYCLES), as a share of the matrix cores' "
+                "busy cycles. Instructions per wave count every wave of the grid, those of empty units "
+                "included (SQ_INSTS_VALU includes the MFMAs).", "",
+                "| kernel | issuing | waiting | waiting for issue | co-execution | MFMA / wave | "
+                "VALU / wave | SALU / wave | LDS / wave | exp / wave |",
+                "|---|---|---|---|---|---|---|---|---|---|"]
+        for k in sorted(issue):
+            if not k.startswith(("attn_", "decode_step")):
+                continue
+            m = {c: _median(v) for c, v in issue[k].items()}
+            wc = max(m.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            nw = max(m.get("SQ_WAVES", 1.0), 1.0)
+            busy = max(m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), 1.0)
+            out.append(f"| {k} | {m.get('SQ_ACTIVE_INST_ANY', 0) / wc:.1%} | {m.get('SQ_WAIT_ANY', 0) / wc:.1%} | "
+                       f"{m.get('SQ_WAIT_INST_ANY', 0) / wc:.1%} | "
+                       f"{m.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0) / busy:.1%} | "
+                       f"{m.get('SQ_INSTS_MFMA', 0) / nw:.0f} | {m.get('SQ_INSTS_VALU', 0) / nw:.0f} | "
+                       f"{m.get('SQ_INSTS_SALU', 0) / nw:.0f} | {m.get('SQ_INSTS_LDS', 0) / nw:.0f} | "
+                       f"{m.get('SQ_INSTS_VALU_TRANS_F32', 0) / nw:.0f} |")
         out.append("")
     print("\n".join(out))
 
