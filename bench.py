@@ -723,7 +723,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 cache, fp32 accumulate" if s.kv_dtype == "bf16" else "fp32",
+        "dtype": "bf16" if s.kv_dtype == "bf16" else "fp32",
+        "accumulate_dtype": "fp32",
         "data": head["data"],
         "config": {"workload": head["workload"], "batch": s.num_seqs, "q_tokens_per_seq": s.q_tokens,
                    "context": int(w.max_seq_len - s.q_tokens), "layers_rotated": head["layers_rotated"],
