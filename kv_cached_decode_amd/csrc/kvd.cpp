@@ -150,7 +150,8 @@ struct Plan {
 // one workgroup per CU when the batch has fewer (sequence, kv head) units
 // than CUs; with more units (continuous batching, ragged lengths) it uses
 // three splits per unit, so the longest-first ordering of the kernel has
-// enough small pieces to balance the CUs.  The VALU kernel targets one round
+// enough small pieces to balance the CUs, but no split shorter than
+// MFMA_MIN_SPLIT_KEYS once the units alone fill the resident slots.  The VALU kernel targets one round
 // of its resident workgroup slots.
 int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) {
     const int D = kv->head_dim;
@@ -210,6 +211,8 @@ int32_t make_plan(const kvd_paged_kv* kv, const kvd_attn_options* opt, Plan* p) 
     } else {
         const int64_t units = (int64_t)kv->num_seqs * kv->n_kv_heads * n_rtiles;
         splits = cdiv(target, units);
+        if (kernel == KVD_KERNEL_MFMA && !p->prefill && units >= kvd::MFMA_WGS_PER_CU * (int64_t)num_cus())
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, max_len / kvd::MFMA_MIN_SPLIT_KEYS));
     }
     splits = std::min<int64_t>(splits, max_splits);
     splits = std::max<int64_t>(splits, cdiv(max_len, max_keys));   // per-split staging limit

@@ -167,6 +167,19 @@ int prefill_step_keys();
 int mfma_step_keys();
 // Workgroups of the decode matrix-core kernel resident on one CU.
 constexpr int MFMA_WGS_PER_CU = 2;
+// Shortest split the matrix-core decode kernel is planned with once the
+// (sequence, kv head) units alone fill every CU's resident slots: a shorter
+// split pays its set-up and its share of the merge for too little streaming,
+// and only ragged batches with long sequences need the pieces to balance.
+// Measured steps (1, 2 and 3 splits, same box), batches of 512 units:
+//   multi-head 16 x 32 kv heads, 4097 keys:  164.3, 168.2, 171.4 us
+//   64 x 8, uniform 2048 keys:               85.6,  97.4, 107.4 us
+//   64 x 8, ragged 1..2048 keys:             63.8,  64.8,  68.4 us
+//   64 x 8, ragged 1..400 keys:              18.4,  28.7,  36.5 us
+//   64 x 8, ragged 129..8193 keys:          232.8, 182.2, 173.6 us
+// so at least 2560 keys a split: one split for the first four, three for
+// the last.
+constexpr int MFMA_MIN_SPLIT_KEYS = 2560;
 // Resident workgroups per CU for a kernel variant (occupancy query on the
 // current device; a conservative default when there is none).
 int valu_wgs_per_cu(int D, int kv_bf16, int row_tile, size_t dyn_lds);

@@ -240,17 +240,19 @@ def test_longest_first_batches(B):
     """Ragged batches whose workgroups exceed the resident slots, so the
     kernel ranks the sequences longest-first: up to 64 sequences inside each
     wave, more through LDS.  Contexts of 1..400 keys, some lengths shared
-    (ties go by index).  The fused step equals the two calls and the oracle."""
+    (ties go by index).  Three splits (the planner gives these short contexts
+    one): the ranking then covers (sequence, split) units.  The fused step
+    equals the two calls and the oracle."""
     spec = workloads.Spec(f"ranked_b{B}", B, 1, 16, 8, 128, 16, "bf16", (1, 400), 10000.0, "normal",
                           "shuffled", spare_frac=0.05, seed=90 + B)
     w = cached_workload(spec)
     note("longest-first batch", B)
     ref_case, case = GpuCase(w), GpuCase(w)
-    splits, _, kern = kb.decode_attention_plan(case.kv)
+    splits, _, kern = kb.decode_attention_plan(case.kv, num_splits=3)
     assert kern == kb.KVD_KERNEL_MFMA and splits * 8 * B > 512, "expected a ranked plan"
     assert len(np.unique(w.seq_lens)) < B, "expected equal lengths"
-    ref = two_calls(ref_case)
-    got = fused(case)
+    ref = two_calls(ref_case, num_splits=3)
+    got = fused(case, num_splits=3)
     assert_same(ref_case, case, ref, got)
     _, out_ref, _, _ = oracle_step(w)
     assert_parity(spec, got[1], out_ref)
