@@ -72,6 +72,7 @@ constexpr int V_BYTES = TILE * VROWB;
 constexpr int MAX_STAGED_BLOCKS = 4096;   // block ids of a split, staged in LDS
 constexpr int RANK_MAX = PREFILL_RANK_MAX;  // units ranked longest-first (their key counts and the units by rank share the block-id array)
 static_assert(RANK_MAX <= THREADS, "one unit per thread in the ranking");
+static_assert(RANK_MAX <= 512 && RANK_MAX % 16 == 0, "unit indices fit the sort key's 9 bits");
 constexpr float M_EMPTY = -1e30f;
 constexpr int HALF = D / 2;
 constexpr int ANG_TOKENS = 32;            // tokens whose angles share the LDS at a time
@@ -240,24 +241,33 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
         // first and the short ones fill the slots at the end.  Every
         // workgroup derives the same permutation; thread v describes unit v
         // and files it under its rank.
-        int* const sm_work = sm_blk;
+        // The sort key packs the key count (below 2^22: a split stages at
+        // most 4094 blocks of at most 1024 keys) above the unit index (a
+        // lower index first among equal counts), so the keys are distinct and
+        // a unit's rank is the number of larger keys: one compare per unit,
+        // sixteen keys per round of four broadcast LDS reads.
+        unsigned* const sm_work = (unsigned*)sm_blk;
         Unit* const sm_unit = (Unit*)(sm_blk + RANK_MAX);
-        const int n4 = (n_units + 3) & ~3;
+        const int n_keys = (n_units + 15) & ~15;
         Unit x{};
-        int w = -1;        // padding: below every unit
+        unsigned key = 0u;        // padding: below every unit
         if (tid < n_units) {
             x = unit_of(a, tid, n_rtiles);
-            w = x.live_rows > 0 ? max(0, x.key_end - x.key_begin) : 0;
+            const int w = x.live_rows > 0 ? max(0, x.key_end - x.key_begin) : 0;
+            key = (unsigned)(w + 1) << 9 | (unsigned)(511 - tid);
         }
-        if (tid < n4) sm_work[tid] = w;
+        if (tid < n_keys) sm_work[tid] = key;
         __syncthreads();
         if (tid < n_units) {
             int r = 0;
-            for (int i = 0; i < n4; i += 4) {
-                const int4 y = *(const int4*)(sm_work + i);
-                r += (y.x > w) + (y.y > w) + (y.z > w) + (y.w > w);
-                r += (y.x == w && i + 0 < tid) + (y.y == w && i + 1 < tid) + (y.z == w && i + 2 < tid) +
-                     (y.w == w && i + 3 < tid);
+            for (int i = 0; i < n_keys; i += 16) {
+                const u32x4 y0 = *(const u32x4*)(sm_work + i);
+                const u32x4 y1 = *(const u32x4*)(sm_work + i + 4);
+                const u32x4 y2 = *(const u32x4*)(sm_work + i + 8);
+                const u32x4 y3 = *(const u32x4*)(sm_work + i + 12);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    r += (y0[e] > key) + (y1[e] > key) + (y2[e] > key) + (y3[e] > key);
             }
             sm_unit[r] = x;
         }
