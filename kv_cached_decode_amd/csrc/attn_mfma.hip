@@ -105,20 +105,42 @@ __device__ inline float xor_sum(float x) {
 // of the grid takes the z-th longest sequence (ties by index).  With a
 // ragged batch the longest units start first and the short ones fill the
 // gaps (longest-processing-time-first list scheduling); a uniform batch keeps
-// its natural order.  Each thread ranks one sequence against all the others
-// (batches up to LPT_MAX_SEQS; larger ones keep their natural order).
-__device__ inline int lpt_rank_pick(int B, int z, const int* sm_len, int* sm_pick) {
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
-        const int Lb = sm_len[b];
+// its natural order.  Batches up to LPT_MAX_SEQS (larger ones keep their
+// natural order): thread b packs sequence b's length with its index into a
+// distinct key (longer first, then lower index; lengths past 2^24 - 1
+// compare as equal, which only changes the order) and counts the keys above
+// its own, sixteen per round of four broadcast LDS reads; the thread of
+// rank z names the sequence.  Returns the sequence and, in len, its length.
+__device__ inline int lpt_rank_pick(int B, int z, const int* seq_lens, unsigned* sm_key, int* sm_pick, int& len) {
+    static_assert(LPT_MAX_SEQS <= 256, "sequence indices fit the key's low 8 bits");
+    const int b = threadIdx.x;          // B <= LPT_MAX_SEQS <= blockDim.x
+    const int n16 = (B + 15) & ~15;
+    const int L = b < B ? seq_lens[b] : 0;
+    const unsigned key = b < B ? (unsigned)min(max(L, 0), (1 << 24) - 1) << 8 | (unsigned)(255 - b) : 0u;
+    if (b < n16) sm_key[b] = key;
+    __syncthreads();
+    if (b < B) {
         int rank = 0;
-        for (int i = 0; i < B; ++i) {
-            const int Li = sm_len[i];
-            rank += (Li > Lb) | ((Li == Lb) & (i < b));
+        for (int i = 0; i < n16; i += 16) {
+            const uint4 y0 = *(const uint4*)(sm_key + i);
+            const uint4 y1 = *(const uint4*)(sm_key + i + 4);
+            const uint4 y2 = *(const uint4*)(sm_key + i + 8);
+            const uint4 y3 = *(const uint4*)(sm_key + i + 12);
+            rank += (y0.x > key) + (y0.y > key) + (y0.z > key) + (y0.w > key);
+            rank += (y1.x > key) + (y1.y > key) + (y1.z > key) + (y1.w > key);
+            rank += (y2.x > key) + (y2.y > key) + (y2.z > key) + (y2.w > key);
+            rank += (y3.x > key) + (y3.y > key) + (y3.z > key) + (y3.w > key);
         }
-        if (rank == z) *sm_pick = b;
+        if (rank == z) {
+            sm_pick[0] = b;
+            sm_pick[1] = L;
+        }
     }
     __syncthreads();
-    return *sm_pick;
+    len = sm_pick[1];
+    const int pick = sm_pick[0];
+    __syncthreads();                    // the ranking's LDS is reused next
+    return pick;
 }
 
 // The same ranking for batches of at most 64 sequences inside one wave: lane
@@ -152,7 +174,7 @@ __device__ inline int lpt_unit_pick(const AttnArgs& a, int pos, unsigned* sm_key
                                     int* sm_len, int& len) {
     const CacheView& c = a.c;
     const int S = a.num_splits;
-    const int n = c.B * S, n4 = (n + 3) & ~3;
+    const int n = c.B * S, n16 = (n + 15) & ~15;     // n <= 256
     const int v = threadIdx.x;
     unsigned key = 0u;                  // padding: below every unit
     int L = 0;
@@ -164,13 +186,20 @@ __device__ inline int lpt_unit_pick(const AttnArgs& a, int pos, unsigned* sm_key
         const int keys = max(0, min(range_end(c, L, qo, n_new(c, bb)), k0 + a.split_keys) - k0);
         key = ((unsigned)min(keys, (1 << 23) - 1) << 8 | (unsigned)(255 - v)) + 1u;
     }
-    if (v < n4) sm_key[v] = key;
+    if (v < n16) sm_key[v] = key;
     __syncthreads();
     if (v < n) {
+        // sixteen keys per round: four broadcast reads in flight
         int r = 0;
-        for (int i = 0; i < n4; i += 4) {
-            const uint4 y = *(const uint4*)(sm_key + i);
-            r += (y.x > key) + (y.y > key) + (y.z > key) + (y.w > key);
+        for (int i = 0; i < n16; i += 16) {
+            const uint4 y0 = *(const uint4*)(sm_key + i);
+            const uint4 y1 = *(const uint4*)(sm_key + i + 4);
+            const uint4 y2 = *(const uint4*)(sm_key + i + 8);
+            const uint4 y3 = *(const uint4*)(sm_key + i + 12);
+            r += (y0.x > key) + (y0.y > key) + (y0.z > key) + (y0.w > key);
+            r += (y1.x > key) + (y1.y > key) + (y1.z > key) + (y1.w > key);
+            r += (y2.x > key) + (y2.y > key) + (y2.z > key) + (y2.w > key);
+            r += (y3.x > key) + (y3.y > key) + (y3.z > key) + (y3.w > key);
         }
         sm_unit[r] = v;
         sm_len[r] = L;
@@ -274,16 +303,15 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     __shared__ int sm_blk[MAX_PIECE_BLOCKS];
     __shared__ float sm_m[WAVES][16];
     __shared__ float sm_l[WAVES][16];
-    __shared__ int sm_pick;
     // fused step: the rounded new K/V rows ([t][dim], bf16 bits), read by the
     // key loop; the query rows, raw then rotated (written to q_rot after the
     // loop); before the loop the V-tile
-    // area holds, after the sequence lengths of the longest-first ranking,
+    // area holds, after the keys of the longest-first ranking,
     // the cos/sin of the new positions' angles ([t][pair])
     __shared__ __attribute__((aligned(16))) uint16_t sm_knew[FUSED ? MAX_T * D : 8];
     __shared__ __attribute__((aligned(16))) uint16_t sm_vnew[FUSED ? MAX_T * D : 8];
     __shared__ __attribute__((aligned(16))) float sm_q[FUSED ? 16 * D : 4];
-    double* const sm_cs = (double*)(sm_v + LPT_MAX_SEQS * 4);   // past the ranking's lengths
+    double* const sm_cs = (double*)(sm_v + LPT_MAX_SEQS * 4);   // past the ranking's keys (ranked first)
     double* const sm_sn = sm_cs + MAX_T * HALF;
     static_assert(LPT_MAX_SEQS * 4 + 2 * MAX_T * HALF * 8 <= WAVES * VT_BYTES,
                   "fused scratch must fit in the V tiles");
@@ -396,11 +424,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
         b = lpt_rank_pick_wave(c.B, z, c.seq_lens, L);
     } else if (ranked) {
         // the ranking borrows the V-tile LDS (unused until the key loop)
-        int* sm_len = (int*)sm_v;
-        for (int i = threadIdx.x; i < c.B; i += blockDim.x) sm_len[i] = c.seq_lens[i];
-        __syncthreads();
-        b = lpt_rank_pick(c.B, z, sm_len, &sm_pick);
-        L = sm_len[b];
+        b = lpt_rank_pick(c.B, z, c.seq_lens, (unsigned*)sm_v, (int*)sm_v + LPT_MAX_SEQS, L);
     }
     const int qo = q_local0(c, b, L);
     if (!early) load_q(b);
