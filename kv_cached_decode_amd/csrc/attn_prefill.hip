@@ -345,7 +345,10 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
 
     // Each thread moves CPT of the 512 16-byte chunks of a K tile and CPT of
     // the V tile: chunk ch = tid + THREADS*i -> key ch / 16, column ch % 16.
-    // Keys past the range re-read its last key (weight 0 below).
+    // Keys past the range re-read its last key (weight 0 below).  Plain
+    // loads, not streaming ones: every row tile of a (sequence, kv head)
+    // reads the same keys at about the same time, and lines loaded with the
+    // streaming hint leave L2 before the other tiles get to them.
     const char* kbase = (const char*)c.k;
     const char* vbase = (const char*)c.v;
     const int bs_mask = (1 << c.log2_bs) - 1;
@@ -358,8 +361,8 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
             const unsigned hrow = sm_blk[(key >> c.log2_bs) - blk0];
             const size_t off = ((size_t)hrow << (c.log2_bs + LOG2_ROW_BYTES)) +
                                ((key & bs_mask) << LOG2_ROW_BYTES | 16 * (ch & 15));
-            kr[i] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
-            vr[i] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
+            kr[i] = *(const u32x4*)(kbase + off);
+            vr[i] = *(const u32x4*)(vbase + off);
         }
     };
     if (!no_keys) load(key_begin);
