@@ -24,6 +24,7 @@ CASES = [
     spec("chunk33_mha", 2, 33, 8, 8, (50, 200), 63),           # g = 1: 33 rows
     spec("ragged_g4", 4, 100, 32, 8, (0, 400), 64, chunk=(0, 100)),
     spec("ragged_bs64", 3, 130, 16, 8, (200, 900), 65, chunk=(17, 130), bs=64),
+    spec("chunk32_g4", 3, 32, 32, 8, (0, 400), 67, chunk=(5, 32)),   # 128 rows: four-wave workgroups
 ]
 
 
