@@ -353,7 +353,29 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
     const char* vbase = (const char*)c.v;
     const int bs_mask = (1 << c.log2_bs) - 1;
     u32x4 kr[CPT], vr[CPT];
+    // When the tiles start on 16-key boundaries of blocks of at least 16
+    // keys, the 16 keys of one chunk row (THREADS / 16 keys apart for the
+    // CPT rows of a thread) share a block: its id is a broadcast LDS read
+    // (all CPT of them issued before the one wait), the address a scalar
+    // base plus the thread's fixed offset (16 * tid), and a whole tile needs
+    // no clamp.
+    static_assert(THREADS / 16 * CPT == TILE, "each chunk row of a tile is THREADS / 16 keys");
+    const bool aligned = c.log2_bs >= 4 && (key_begin & 15) == 0;
     auto load = [&](int base) {
+        if (aligned && base + TILE <= key_end) {
+            unsigned hrow[CPT];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) hrow[i] = sm_blk[((base + THREADS / 16 * i) >> c.log2_bs) - blk0];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int kb = base + THREADS / 16 * i;
+                const size_t off = ((size_t)__builtin_amdgcn_readfirstlane(hrow[i]) << (c.log2_bs + LOG2_ROW_BYTES)) +
+                                   ((size_t)(kb & bs_mask) << LOG2_ROW_BYTES);
+                kr[i] = *(const u32x4*)(kbase + off + (unsigned)(16 * tid));
+                vr[i] = *(const u32x4*)(vbase + off + (unsigned)(16 * tid));
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int ch = tid + THREADS * i;
