@@ -674,7 +674,7 @@ def main():
         summarize(args.summarize, args.workload, args.command, record=args.kernel == 0)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence, kv head or key range with no exchange inside the "
               "attention step; see the design notes)", file=sys.stderr)
         sys.exit(2)

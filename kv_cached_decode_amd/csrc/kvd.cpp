@@ -385,8 +385,8 @@ int32_t attention(const kvd_paged_kv* kv, const float* q_rot, float* out, float*
         a.part_ml = (float*)((char*)workspace + cv.ml);
         // with two splits the decode kernel merges them itself (the last
         // workgroup of a (sequence, kv head) to finish); otherwise the
-        // partials go to the combine kernel.  Measured (median step, same
-        // box, the two alternating): two splits, Llama-3-8B-shaped layer
+        // partials go to the combine kernel.  Measured (median step, one
+        // GPU, the two alternating): two splits, Llama-3-8B-shaped layer
         // 47.6 -> 46.95 us with the merge in the kernel; three splits (the
         // continuous batch) 173.4 against 174.2 us and eight (131k context)
         // 323.9 against 326.2 us in favour of the combine kernel: the last

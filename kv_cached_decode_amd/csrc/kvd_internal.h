@@ -171,7 +171,7 @@ constexpr int MFMA_WGS_PER_CU = 2;
 // (sequence, kv head) units alone fill every CU's resident slots: a shorter
 // split pays its set-up and its share of the merge for too little streaming,
 // and only ragged batches with long sequences need the pieces to balance.
-// Measured steps (1, 2 and 3 splits, same box), batches of 512 units:
+// Measured steps (1, 2 and 3 splits, one GPU), batches of 512 units:
 //   multi-head 16 x 32 kv heads, 4097 keys:  164.3, 168.2, 171.4 us
 //   64 x 8, uniform 2048 keys:               85.6,  97.4, 107.4 us
 //   64 x 8, ragged 1..2048 keys:             63.8,  64.8,  68.4 us
