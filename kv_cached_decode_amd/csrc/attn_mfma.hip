@@ -161,6 +161,18 @@ __device__ inline int lpt_rank_pick_wave(int B, int z, const int* seq_lens, int&
     return pick;
 }
 
+// Split s of S over the keys [rs, re) one sequence's queries see, in equal
+// shares of that range (ragged batches, where the units are ranked by key
+// count: a split of the plan's length, split_keys, would leave a short
+// sequence one piece and empty splits beside it): [k0, k1), empty when the
+// range has fewer than s + 1 keys.  Each share is at most split_keys, since
+// the range is at most the plan's length.
+__device__ inline void equal_split(int rs, int re, int S, int s, int& k0, int& k1) {
+    const int e = max(1, (re - rs + S - 1) / S);
+    k0 = rs + s * e;
+    k1 = min(re, k0 + e);
+}
+
 // Unit order, when the batch has several splits: the units are (sequence,
 // split) pairs, and a split of a short sequence can hold as many keys as a
 // split of a long one, so the units themselves are ranked.  Thread v (one
@@ -182,8 +194,9 @@ __device__ inline int lpt_unit_pick(const AttnArgs& a, int pos, unsigned* sm_key
         const int bb = v / S, s = v - bb * S;
         L = c.seq_lens[bb];
         const int qo = q_local0(c, bb, L);
-        const int k0 = range_start(c, qo) + s * a.split_keys;
-        const int keys = max(0, min(range_end(c, L, qo, n_new(c, bb)), k0 + a.split_keys) - k0);
+        int k0, k1;
+        equal_split(range_start(c, qo), range_end(c, L, qo, n_new(c, bb)), S, s, k0, k1);
+        const int keys = max(0, k1 - k0);
         key = ((unsigned)min(keys, (1 << 23) - 1) << 8 | (unsigned)(255 - v)) + 1u;
     }
     if (v < n16) sm_key[v] = key;
@@ -224,8 +237,8 @@ constexpr int PER_THREAD = 16 * D / 256;     // (row, dim) elements of a workgro
 // agent-scope loads -- so the result does not depend on which split finished
 // last.  Rows of padding tokens are left as they are.
 __device__ __forceinline__ void merge_own_splits(const AttnArgs& a, int b, int kvh, int split, int nn, int first_key,
-                                 int rend, const float (&own_o)[PER_THREAD], const float (&own_m)[PER_THREAD],
-                                 const float (&own_l)[PER_THREAD]) {
+                                 int rend, int split_len, const float (&own_o)[PER_THREAD],
+                                 const float (&own_m)[PER_THREAD], const float (&own_l)[PER_THREAD]) {
     const CacheView& c = a.c;
     __shared__ unsigned sm_ticket;
     __builtin_amdgcn_s_waitcnt(0);          // every counter at zero: this thread's stores are done
@@ -237,7 +250,7 @@ __device__ __forceinline__ void merge_own_splits(const AttnArgs& a, int b, int k
     if (sm_ticket != (unsigned)(S - 1)) return;
     if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // splits s >= live hold no key of the sequence
-    const int live = rend > first_key ? min(S, (rend - first_key + a.split_keys - 1) / a.split_keys) : 0;
+    const int live = rend > first_key ? min(S, (rend - first_key + split_len - 1) / split_len) : 0;
     constexpr int MAXS = 8;                 // up to this many splits, every load goes out at once
 #pragma unroll
     for (int k = 0; k < PER_THREAD; ++k) {
@@ -346,10 +359,12 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     float xq[4][8];
     int tb[MAX_PIECE_BLOCKS / 256];
     float kx = 0.0f, ky = 0.0f, vx = 0.0f, vy = 0.0f;
-    // qo: local index of the position of the sequence's first new token
-    auto split_begin = [&](int qo) { return range_start(c, qo) + split * a.split_keys; };
+    // qo: local index of the position of the sequence's first new token.
+    // The split's first key (set below) and its length: the plan's, or an
+    // equal share of the sequence's range when the units are ranked.
+    int split_key0 = 0, split_len = a.split_keys;
     auto new_pair = [&](int bb, int qo, int idx, int& ia, int& ic, size_t& src) {
-        const int n0 = max(qo, split_begin(qo));
+        const int n0 = max(qo, split_key0);
         const int t = n0 + idx / HALF - qo;
         rope_pair(idx % HALF, HALF, a.interleaved, ia, ic);
         src = (((size_t)bb * c.T + t) * c.Hkv + kvh) * D;
@@ -429,8 +444,14 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     const int qo = q_local0(c, b, L);
     if (!early) load_q(b);
     const int nn = n_new(c, b);          // new tokens of this sequence (rows past them: padding)
-    const int key_begin = split_begin(qo);
     const int rend = range_end(c, L, qo, nn);
+    int key_begin = range_start(c, qo) + split * a.split_keys;
+    if (ranked && a.num_splits > 1) {
+        int k1;
+        equal_split(range_start(c, qo), rend, a.num_splits, split, key_begin, k1);
+        split_len = max(1, (rend - range_start(c, qo) + a.num_splits - 1) / a.num_splits);
+    }
+    split_key0 = key_begin;
     const bool self_merge = a.num_splits > 1 && a.counters;
     if (key_begin >= rend) {            // empty split
         if (self_merge) {
@@ -441,13 +462,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
                 own_m[k] = M_EMPTY;
                 own_l[k] = 0.0f;
             }
-            merge_own_splits(a, b, kvh, split, nn, range_start(c, qo), rend, own_o, own_m, own_l);
+            merge_own_splits(a, b, kvh, split, nn, range_start(c, qo), rend, split_len, own_o, own_m, own_l);
         } else {
             write_empty_partials(a, b, kvh, split, 0, a.rows);
         }
         return;
     }
-    const int key_end = min(rend, key_begin + a.split_keys);
+    const int key_end = min(rend, key_begin + split_len);
     if (!early) load_blocks(b, key_begin);
     // first new token this split holds (if any): the early pair assumed 0
     const int t0 = max(qo, key_begin) - qo;
@@ -816,7 +837,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
             if (t < nn) a.q_rot[(((size_t)b * c.T + t) * c.Hq + kvh * c.g + (r - t * c.g)) * D + d] = sm_q[idx];
         }
 
-    if (self_merge) merge_own_splits(a, b, kvh, split, nn, range_start(c, qo), rend, own_o, own_m, own_l);
+    if (self_merge) merge_own_splits(a, b, kvh, split, nn, range_start(c, qo), rend, split_len, own_o, own_m, own_l);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) { attn_mfma_body<false>(a); }

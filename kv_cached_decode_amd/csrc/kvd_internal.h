@@ -38,7 +38,8 @@ __device__ inline int q_local0(const CacheView& c, int b, int L) {
 // Keys any query of a sequence can see: [range_start, range_end), from the
 // start of the first query's window (0 without one) to the last query's
 // position.  Split s covers [range_start + s*split_keys, min(range_end,
-// range_start + (s+1)*split_keys)).
+// range_start + (s+1)*split_keys)), except in the matrix-core decode kernel
+// when it ranks its units, where the S splits are equal shares of the range.
 __device__ inline int range_start(const CacheView& c, int qo) {
     return c.window > 0 ? max(0, qo - c.window + 1) : 0;
 }
