@@ -84,3 +84,31 @@ def test_merge_in_the_fused_step_through_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i} differs from the eager step"
         assert not ws[:kb.WORKSPACE_COUNTER_BYTES].any()
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+def test_ranked_batch_equal_shares(splits):
+    """The continuous batch at full size with more (sequence, split) units
+    than resident slots: the kernel ranks them and gives each sequence's
+    splits equal shares of its own key range.  With two splits it merges
+    them itself (its live splits counted from that share), with four the
+    combine kernel does; both equal the one-split result (an unranked plan
+    over whole sequences), lse included, through repeated calls."""
+    w = cached_workload(workloads.CONFIGS["qwen3_0_6b_cb"])
+    note("ranked equal shares", splits)
+    case = GpuCase(w)
+    kv = case.kv
+    assert kb.decode_attention_plan(kv, splits, kb.KVD_KERNEL_MFMA)[0] == splits
+    n = kb.decode_attention_workspace_size(kv, splits, kb.KVD_KERNEL_MFMA)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(100 + splits)
+    for i in range(3):
+        q = torch.randn(kv.q_shape(), generator=g, device=DEV) * (1.0 + 3.0 * i)
+        out, lse = kb.decode_attention_lse(kv, q, workspace_buf=ws, num_splits=splits, kernel=kb.KVD_KERNEL_MFMA)
+        again = kb.decode_attention(kv, q, workspace_buf=ws, num_splits=splits, kernel=kb.KVD_KERNEL_MFMA)
+        one, lse1 = kb.decode_attention_lse(kv, q, num_splits=1, kernel=kb.KVD_KERNEL_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again), f"call {i}: not deterministic"
+        assert _close(out, one), f"call {i}: split shares differ from one split"
+        assert torch.allclose(lse, lse1, rtol=1e-5, atol=1e-5), f"call {i}: lse differs"
+        assert not ws[:kb.WORKSPACE_COUNTER_BYTES].any(), f"call {i}: counters left nonzero"
