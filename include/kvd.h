@@ -189,7 +189,9 @@ size_t kvd_decode_attention_workspace_size_ex(const kvd_paged_kv *kv,
                                               const kvd_attn_options *opt);
 
 /* The plan kvd_decode_attention would use: key-range partitions per (seq, kv
- * head), keys per partition and kernel family.  Any out pointer may be NULL.
+ * head), keys per partition (at most; on a ragged batch whose units the
+ * matrix-core decode kernel ranks, each sequence's partitions are equal
+ * shares of its own range) and kernel family.  Any out pointer may be NULL.
  * The pages define no such call (the Ferrum Infer README only says split-K
  * switches on for long caches); it reports this library's choice. */
 int32_t kvd_decode_attention_plan(const kvd_paged_kv *kv, const kvd_attn_options *opt,
