@@ -165,12 +165,15 @@ __device__ inline int lpt_rank_pick_wave(int B, int z, const int* seq_lens, int&
 // shares of that range (ragged batches, where the units are ranked by key
 // count: a split of the plan's length, split_keys, would leave a short
 // sequence one piece and empty splits beside it): [k0, k1), empty when the
-// range has fewer than s + 1 keys.  Each share is at most split_keys, since
-// the range is at most the plan's length.
-__device__ inline void equal_split(int rs, int re, int S, int s, int& k0, int& k1) {
-    const int e = max(1, (re - rs + S - 1) / S);
+// range has fewer than s + 1 keys.  A share is at most split_keys (the
+// range is at most the plan's length; a sequence longer than max_seq_len,
+// outside the contract, keeps the plan's split length and loses its last
+// keys, as with the plan's splits).  Returns the share.
+__device__ inline int equal_split(int rs, int re, int S, int s, int split_keys, int& k0, int& k1) {
+    const int e = min(split_keys, max(1, (re - rs + S - 1) / S));
     k0 = rs + s * e;
     k1 = min(re, k0 + e);
+    return e;
 }
 
 // Unit order, when the batch has several splits: the units are (sequence,
@@ -195,7 +198,7 @@ __device__ inline int lpt_unit_pick(const AttnArgs& a, int pos, unsigned* sm_key
         L = c.seq_lens[bb];
         const int qo = q_local0(c, bb, L);
         int k0, k1;
-        equal_split(range_start(c, qo), range_end(c, L, qo, n_new(c, bb)), S, s, k0, k1);
+        equal_split(range_start(c, qo), range_end(c, L, qo, n_new(c, bb)), S, s, a.split_keys, k0, k1);
         const int keys = max(0, k1 - k0);
         key = ((unsigned)min(keys, (1 << 23) - 1) << 8 | (unsigned)(255 - v)) + 1u;
     }
@@ -448,8 +451,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a) {
     int key_begin = range_start(c, qo) + split * a.split_keys;
     if (ranked && a.num_splits > 1) {
         int k1;
-        equal_split(range_start(c, qo), rend, a.num_splits, split, key_begin, k1);
-        split_len = max(1, (rend - range_start(c, qo) + a.num_splits - 1) / a.num_splits);
+        split_len = equal_split(range_start(c, qo), rend, a.num_splits, split, a.split_keys, key_begin, k1);
     }
     split_key0 = key_begin;
     const bool self_merge = a.num_splits > 1 && a.counters;
