@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import DEV, GpuCase, cached_workload, note
+from gpu_common import DEV, GpuCase, assert_parity, cached_workload, note, oracle_step
 from kv_cached_decode_amd import binding as kb
 from kv_cached_decode_amd import workloads
 
@@ -112,3 +112,24 @@ def test_ranked_batch_equal_shares(splits):
         assert _close(out, one), f"call {i}: split shares differ from one split"
         assert torch.allclose(lse, lse1, rtol=1e-5, atol=1e-5), f"call {i}: lse differs"
         assert not ws[:kb.WORKSPACE_COUNTER_BYTES].any(), f"call {i}: counters left nonzero"
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+def test_ranked_batch_equal_shares_with_window(splits):
+    """The ranked continuous batch with a sliding window of 3000 keys: each
+    sequence's splits share its windowed range equally.  The two-call step
+    and the fused step (new K/V substituted from the split holding them)
+    against the oracle, every row."""
+    spec = workloads.CONFIGS["qwen3_0_6b_cb"]
+    w = cached_workload(spec)
+    window = 3000
+    note("ranked equal shares, window", splits)
+    case = GpuCase(w, window=window)
+    kv = case.kv
+    assert kb.decode_attention_plan(kv, splits, kb.KVD_KERNEL_MFMA)[0] == splits
+    _, out = case.step(num_splits=splits)
+    _, ref, _, _ = oracle_step(w, window=window)
+    assert_parity(spec, out, ref, label=f"ranked window two-call/{splits}")
+    fused = kb.decode_step(kv, case.q, case.k, case.v, rope_base=spec.rope_base, num_splits=splits)
+    torch.cuda.synchronize()
+    assert_parity(spec, fused.cpu().numpy(), ref, label=f"ranked window fused/{splits}")
