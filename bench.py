@@ -472,7 +472,8 @@ def _median(v):
 def summarize(prof_dir, workload, commands, record=True):
     """Turn rocprofv3 CSV output (kt/ kernel trace, fetch/ FETCH_SIZE,
     write/ WRITE_SIZE, util/ utilisation counters, tcc/ L2 hits and misses,
-    mix/ request sizes, issue/ and insts/ issue, stall and instruction counts)
+    mix/ request sizes, issue/ and insts/ issue, stall and instruction counts,
+    mops/ matrix-core operations)
     into a markdown summary on stdout and, with `record` (runs of the
     automatic plan), record the calibrated traffic per call."""
     import collections
@@ -592,6 +593,34 @@ def summarize(prof_dir, workload, commands, record=True):
                        f"{m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / 1024 / cyc:.2%} | "
                        f"{m.get('SQ_INSTS_VALU', 0) / max(m.get('SQ_WAVES', 1), 1):.0f} | "
                        f"{m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+        out.append("")
+
+    # matrix-core work: SQ_INSTS_VALU_MFMA_MOPS_* count in units of 512 flops
+    # (32 for one 16x16x32 instruction)
+    mops = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv_rows(os.path.join(prof_dir, "mops"), "counter_collection.csv"):
+        mops[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if mops:
+        aflops = w.algorithmic_flops()
+        out += ["## Matrix-core work (--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 "
+                "SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE)", "",
+                "The MOPS counters count matrix-core work in units of 512 flops (32 per 16x16x32 "
+                "instruction). The rate divides by the kernel's median duration above; the last column "
+                f"compares with the attention's algorithmic {aflops / 1e9:.2f} GFLOP (q.K and the "
+                "weighted V sum of every real query row over the keys it sees).", "",
+                "| kernel | bf16 GFLOP | fp16 GFLOP | fp32 GFLOP | TFLOP/s at the median duration | "
+                "matrix-core / algorithmic flops |", "|---|---|---|---|---|---|"]
+        for k in sorted(mops):
+            if not k.startswith(("attn_", "decode_step")) or k not in ours:
+                continue
+            m = {c: _median(v) * 512 for c, v in mops[k].items()}
+            tot = sum(m.get(f"SQ_INSTS_VALU_MFMA_MOPS_{t}", 0.0) for t in ("BF16", "F16", "F32"))
+            if tot == 0:
+                continue
+            out.append(f"| {k} | {m.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0) / 1e9:.2f} | "
+                       f"{m.get('SQ_INSTS_VALU_MFMA_MOPS_F16', 0) / 1e9:.2f} | "
+                       f"{m.get('SQ_INSTS_VALU_MFMA_MOPS_F32', 0) / 1e9:.2f} | "
+                       f"{tot / (_median(ours[k]) * 1e-6) / 1e12:.1f} | {tot / aflops:.2f}x |")
         out.append("")
 
     # where the waves' time goes: issuing, waiting on a counter (s_waitcnt,
