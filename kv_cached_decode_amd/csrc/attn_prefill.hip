@@ -234,6 +234,9 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
     const int pos = blockIdx.x / c.Hkv;
     const int n_rtiles = (a.rows + ROWS - 1) / ROWS;
     const int n_units = a.num_splits * n_rtiles * c.B;
+    // the rotation pair's frequency, read first: the ranking's waits cover
+    // it, so the angle rounds below wait for no load
+    const double theta = a.rope_q ? kernarg_double(offsetof(AttnArgs, theta), tid % HALF) : 0.0;
     Unit un;
     if (a.rank_longest && n_units <= RANK_MAX) {
         // Longest-first: position pos takes the unit of rank pos by key count
@@ -277,6 +280,9 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
     } else {
         un = unit_of(a, pos, n_rtiles);
     }
+    // theta has arrived by now (the unit's own loads were waited for); a
+    // counted wait says so, so that the angle loop waits for no later load
+    __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
     const int b = un.b, split = un.split;
     const int row0 = un.rtile * ROWS;
     const int qo = un.qo, n_live = un.n_live, live_rows = un.live_rows;
@@ -315,10 +321,26 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
         lo[rb] = c.window > 0 ? vis[rb] - c.window + 1 : 0;
     }
 
+    // The rotation's tokens: t_lo .. t_hi - 1 cover the tile's live rows;
+    // row block rb of this lane holds token t_row[rb] (-1 past the chunk).
+    // pos0 is the global position of the sequence's token 0.
+    const int t_lo = row0 / c.g;
+    const int t_hi = min(n_live - 1, row0 + ROWS - 1) / c.g + 1;
+    const int pos0 = a.rope_q ? qo + (c.key_pos0 ? c.key_pos0[b] : 0) : 0;
+    double* const cs = (double*)sm_kv;       // the angles, before the first tile is staged
+    double* const sn = cs + ANG_TOKENS * HALF;
+    // the angles of tokens tb .. tb + nt - 1 into LDS (thread tid keeps pair
+    // tid % HALF in every round)
+    auto angles = [&](int tb, int nt) {
+        for (int idx = tid; idx < nt * HALF; idx += THREADS)
+            rope_angle(theta, pos0 + tb + idx / HALF, cs[idx], sn[idx]);
+    };
+
     // This lane's query elements (dims 32kk + 8j .. +8 of each row; rows past
     // the chunk take zeros, their results are replaced below) and the
-    // split's block ids are fetched together; the first K/V tile's loads go
-    // out once the block ids are in LDS.
+    // split's block ids are fetched together, and the first round of the
+    // rotation's angles is formed while they are in flight; the first K/V
+    // tile's loads go out once the block ids are in LDS.
     float4 xq[RB][4][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -335,8 +357,12 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
     const int blk0 = key_begin >> c.log2_bs;
     const int nblk = no_keys ? 0 : ((key_end - 1) >> c.log2_bs) - blk0 + 1;
     const int* trow = c.table + (size_t)b * c.max_blocks + blk0;
-    // staged as the (block, kv head) row of the pools: blk * Hkv + kvh
-    for (int i = tid; i < nblk; i += blockDim.x) sm_blk[i] = trow[i] * c.Hkv + kvh;
+    // staged as the (block, kv head) row of the pools: blk * Hkv + kvh; each
+    // thread's first id is read before the angles
+    const int blk_pre = tid < nblk ? trow[tid] : 0;
+    if (a.rope_q) angles(t_lo, min(ANG_TOKENS, t_hi - t_lo));
+    if (tid < nblk) sm_blk[tid] = blk_pre * c.Hkv + kvh;
+    for (int i = tid + THREADS; i < nblk; i += THREADS) sm_blk[i] = trow[i] * c.Hkv + kvh;
     if (tid == 0) {
         sm_v_normal = 0;
         sm_nonfinite = 0;
@@ -391,22 +417,15 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
 
     if (a.rope_q) {
         // The queries of the tile's tokens, rotated at their positions: the
-        // angles of up to ANG_TOKENS tokens at a time into LDS (thread tid
-        // keeps pair tid % HALF in every round), then each lane turns the
-        // pairs of its rows whose tokens are in the round.
-        double* const cs = (double*)sm_kv;
-        double* const sn = cs + ANG_TOKENS * HALF;
-        const double theta = kernarg_double(offsetof(AttnArgs, theta), tid % HALF);
-        const int pos0 = qo + (c.key_pos0 ? c.key_pos0[b] : 0);    // global position of token 0
-        const int t_lo = row0 / c.g;
-        const int t_hi = min(n_live - 1, row0 + ROWS - 1) / c.g + 1;
+        // angles of up to ANG_TOKENS tokens at a time in LDS (the first
+        // round's are there already), then each lane turns the pairs of its
+        // rows whose tokens are in the round.
         int t_row[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) t_row[rb] = row_live[rb] ? (wrow0 + 16 * rb + n16) / c.g : -1;
         for (int tb = t_lo; tb < t_hi; tb += ANG_TOKENS) {
             const int nt = min(ANG_TOKENS, t_hi - tb);
-            for (int idx = tid; idx < nt * HALF; idx += blockDim.x)
-                rope_angle(theta, pos0 + tb + idx / HALF, cs[idx], sn[idx]);
+            if (tb != t_lo) angles(tb, nt);
             __syncthreads();
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
