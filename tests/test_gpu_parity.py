@@ -64,6 +64,23 @@ def test_full_configs_all_rows(spec):
 
 
 @needs_gpu
+@pytest.mark.parametrize("name", ["llama3_8b", "qwen3_0_6b_cb", "long_ctx", "llama2_7b_mha"])
+def test_valu_kernel_full_configs(name):
+    """The vector-ALU kernel (the family of fp32 caches and head dims other
+    than 128) forced onto the full bf16 configurations, as its profiles time
+    it, with its own automatic split plan: every output row against the
+    oracle."""
+    spec = workloads.CONFIGS[name]
+    w = cached_workload(spec)
+    case = GpuCase(w)
+    note("valu full", name, "plan", kb.decode_attention_plan(case.kv, kernel=kb.KVD_KERNEL_VALU))
+    _, out = case.step(kernel=kb.KVD_KERNEL_VALU)
+    _, ref, _, _ = oracle_step(w)
+    e = assert_parity(spec, out, ref, label=f"valu_full/{name}")
+    print(f"{name} (vector ALU): error {e:.3e} on every row")
+
+
+@needs_gpu
 def test_tiny_config_append_chain():
     """Tiny fp32 configuration: 32 GPU appends at positions 0..31, then the
     decode step at position 32; pools and output against the oracle's chain and
