@@ -322,7 +322,6 @@ __global__ __launch_bounds__(THREADS, PREFILL_WGS_PER_CU) void attn_prefill_kern
     }
 
     // The rotation's tokens: t_lo .. t_hi - 1 cover the tile's live rows;
-    // row block rb of this lane holds token t_row[rb] (-1 past the chunk).
     // pos0 is the global position of the sequence's token 0.
     const int t_lo = row0 / c.g;
     const int t_hi = min(n_live - 1, row0 + ROWS - 1) / c.g + 1;
