@@ -62,7 +62,11 @@ constexpr int TILE = 32;
 constexpr int RB = 2;                     // 16-row blocks per wave
 constexpr int WROWS = 16 * RB;            // query rows per wave
 constexpr int ROWS = WAVES * WROWS;       // query rows per workgroup
-constexpr int KROWB = D * 2 + 16;         // LDS row stride of the K tile: 16 rows read at one column hit distinct banks
+// LDS row stride of the K tile, 288 bytes as for the V tile: the tile's reads
+// and writes are then free of bank conflicts (SQ_LDS_BANK_CONFLICT per
+// dispatch of the chunked prefill: 51k at 288 bytes, 6.3M at 272 and 320,
+// 44M at 256)
+constexpr int KROWB = D * 2 + 32;
 constexpr int VROWB = D * 2 + 32;         // LDS row stride of the V tile (transposed reads)
 constexpr int CHUNKS = TILE * D * 2 / 16;   // 16-byte chunks of a K (or V) tile
 constexpr int CPT = CHUNKS / THREADS;        // of them per thread
