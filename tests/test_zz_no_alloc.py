@@ -24,7 +24,8 @@ def with_workspace(case, splits):
     s = case.w.spec
     n = kb.decode_attention_workspace_size(case.kv, splits)
     ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=case.q.device)
-    out, q_rot = torch.empty_like(case.q), torch.zeros_like(case.q)
+    # zeroed: the rows of padding tokens (ragged chunks) are left as they are
+    out, q_rot = torch.zeros_like(case.q), torch.zeros_like(case.q)
     kb.decode_step(case.kv, case.q, case.k, case.v, out=out, q_rot=q_rot, rope_base=s.rope_base,
                    layout=s.layout, workspace_buf=ws, num_splits=splits)
     torch.cuda.synchronize()
@@ -33,7 +34,8 @@ def with_workspace(case, splits):
 
 def no_alloc(case, splits):
     s = case.w.spec
-    out, q_rot = torch.empty_like(case.q), torch.zeros_like(case.q)
+    # zeroed: the rows of padding tokens (ragged chunks) are left as they are
+    out, q_rot = torch.zeros_like(case.q), torch.zeros_like(case.q)
     kb.decode_step_noalloc(case.kv, case.q, case.k, case.v, out, q_rot=q_rot, rope_base=s.rope_base,
                            layout=s.layout, num_splits=splits)
     torch.cuda.synchronize()
@@ -88,3 +90,36 @@ def test_no_alloc_rejects_a_plan_beyond_the_scratch():
     torch.cuda.synchronize()
     for a, b in zip(before, case.pools()):
         assert np.array_equal(bits(a), bits(b))
+
+
+def test_no_alloc_prefill_step_with_splits():
+    """A chunked-prefill plan (ragged chunks, RoPE of the queries inside the
+    prefill kernel) at 2 and then 3 forced splits, its partials in the static
+    scratch: bit for bit the step with a workspace, then against the oracle."""
+    # two sequences, ragged chunks of up to 48 tokens (192 query rows per kv
+    # head: two row tiles of the prefill kernel); 3.2 and 4.8 MB of partials
+    spec = workloads.small_variant("chunked_prefill").with_(name="chunked_prefill_noalloc", num_seqs=2,
+                                                            q_tokens=48, chunk=(1, 48), seed=109)
+    w = cached_workload(spec)
+    for splits in (2, 3):
+        note("no-alloc prefill step", spec.name, "splits", splits)
+        ref_case, case = GpuCase(w), GpuCase(w)
+        assert kb.decode_attention_plan(case.kv, splits)[0] == splits
+        need = kb.decode_attention_workspace_size(case.kv, splits)
+        assert 0 < need <= kb.NOALLOC_SCRATCH_BYTES, need
+        ref = with_workspace(ref_case, splits)
+        got = no_alloc(case, splits)
+        assert np.array_equal(bits(ref[0]), bits(got[0])), "output differs from kvd_decode_step"
+        assert np.array_equal(bits(ref[1]), bits(got[1])), "rotated queries differ"
+        for a, b in zip(ref_case.pools(), case.pools()):
+            assert np.array_equal(bits(a), bits(b)), "cache pools differ"
+        q_ref, out_ref, kp_ref, vp_ref = oracle_step(w)
+        kp, vp = case.pools()
+        assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref)
+        live = np.zeros(out_ref.shape[:2], bool)
+        for b, n in enumerate(w.q_lens):
+            live[b, :n] = True
+        assert_qrot(got[1][live], q_ref[live])
+        assert_parity(spec, got[0][live], out_ref[live], label=f"noalloc/{spec.name}/{splits}")
+        del ref_case, case
+        torch.cuda.empty_cache()
